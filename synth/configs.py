@@ -1,0 +1,77 @@
+"""The five MoE workloads the layer is built and measured on.
+
+Shapes follow the configurations the method's pages motivate:
+ * a tiny gated SwiGLU MoE (correctness case);
+ * a decode-sized bf16 gated MoE (weight streaming, HBM bound);
+ * a fp8 W8A8 MoE with 128x128 block scales and the shared expert fused as
+   an extra expert slot (the Qwen3-Next page, "Shared-Expert Fusion");
+ * a non-gated relu^2 fp8 per-tensor MoE (the NemotronH / TRTLLM-Gen page,
+   "non-gated activation" and the intermediate padding to 128);
+ * a prefill-sized W4A8 MoE, one GPU's share of 160 experts (the GLM W4A8
+   grouped GEMM page).
+"""
+from dataclasses import dataclass
+from typing import Tuple
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    cid: int
+    name: str
+    H: int            # hidden size
+    I: int            # intermediate size per expert (already aligned)
+    E_routed: int     # routed experts (columns of the router logits)
+    top_k: int        # routed slots per token
+    n_shared: int     # shared-expert slots appended after the routed ones
+    shared_gate: float
+    act: str          # "silu" (gated SiLU*up) or "relu2" (non-gated relu(x)^2)
+    quant: str        # "bf16" | "fp8_tensor" | "fp8_block" | "w4a8"
+    renormalize: bool
+    Ms: Tuple[int, ...]
+    a2_const: float = 0.0   # static intermediate activation scale (fp8 / w4a8)
+
+    @property
+    def E(self) -> int:
+        return self.E_routed + self.n_shared
+
+    @property
+    def K_slots(self) -> int:
+        return self.top_k + self.n_shared
+
+    @property
+    def gated(self) -> bool:
+        return self.act == "silu"
+
+    @property
+    def N1(self) -> int:
+        """Rows of the up-projection weight per expert (2I gated, I otherwise)."""
+        return 2 * self.I if self.gated else self.I
+
+
+CONFIGS = {
+    1: MoEConfig(1, "tiny_gated_bf16", H=256, I=512, E_routed=8, top_k=2,
+                 n_shared=0, shared_gate=1.0, act="silu", quant="bf16",
+                 renormalize=True, Ms=(64,)),
+    2: MoEConfig(2, "decode_bf16_gated", H=2048, I=768, E_routed=128, top_k=8,
+                 n_shared=0, shared_gate=1.0, act="silu", quant="bf16",
+                 renormalize=True, Ms=(1, 8, 32, 64)),
+    3: MoEConfig(3, "fp8_block128_shared", H=2048, I=512, E_routed=512, top_k=10,
+                 n_shared=1, shared_gate=1.0, act="silu", quant="fp8_block",
+                 renormalize=True, Ms=(16, 256, 4096)),
+    # relu(h)^2 with h ~ N(0,1): a static a2 of 32/448 puts the e4m3 range
+    # limit at h ~ 5.7, i.e. ~1e-8 of the intermediate values saturate.
+    4: MoEConfig(4, "fp8_tensor_relu2", H=4096, I=2688, E_routed=128, top_k=6,
+                 n_shared=0, shared_gate=1.0, act="relu2", quant="fp8_tensor",
+                 renormalize=True, Ms=(1, 128, 8192), a2_const=32.0 / 448.0),
+    # silu(g)*u with g, u ~ N(0,1): |a| beyond 24 is rarer than 1e-9.
+    5: MoEConfig(5, "w4a8_prefill", H=6144, I=1536, E_routed=20, top_k=8,
+                 n_shared=0, shared_gate=1.0, act="silu", quant="w4a8",
+                 renormalize=True, Ms=(8192,), a2_const=24.0 / 448.0),
+}
+
+
+def config_by_name(name: str) -> MoEConfig:
+    for c in CONFIGS.values():
+        if c.name == name:
+            return c
+    raise KeyError(name)
