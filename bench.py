@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Throughput of the fused MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload cfg2_M64] [--gpus 1]
+
+One step is one whole pass of the layer -- route, align, (fp8 quantise),
+GEMM1 + activation, GEMM2 + combine -- over one batch of synthetic tokens
+already resident in HBM, issued as the C-ABI entry points on the current HIP
+stream (the same sequence moe_forward runs).  The default workload is the
+decode-sized bf16 gated MoE (hidden 2048, 128 experts, top-8, intermediate
+768) at M = 64 tokens.  K steps are timed back to back between two device
+synchronisations; HIP events recorded on the same stream around each entry
+point give the per-kernel durations for the roofline of the dominant kernel
+(GEMM1, which streams two thirds of the weight bytes).
+
+Printed: one JSON line.  ``roofline`` relates GEMM1's algorithmic bytes
+(W13 of the experts the batch routes to, the tokens' hidden rows and the
+half-width intermediate it writes) to its measured time and the 8 TB/s HBM
+peak; ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
+workload on the host cores; ``sweep`` gives every token count of the
+configuration, each pass timed alone after evicting the caches.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+METRIC = "MoE layer tokens/s + % HBM roofline (M≤64) / % MFMA peak (M≥4096)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="cfg2_M64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for counter scaling)")
+    return ap.parse_args()
+
+
+def workload(name):
+    import synth
+    cid, m = name.split("_M")
+    return synth.CONFIGS[int(cid.replace("cfg", ""))], int(m)
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+        else torch.from_numpy(a)
+    return t.to("cuda")
+
+
+def make_layer(cfg, W, a1, a2):
+    import torch
+    from mixture_experts_layer_09_amd.layer import MoELayer
+    sc = lambda v: None if v is None else torch.tensor(float(v), dtype=torch.float32,
+                                                       device="cuda")
+    return MoELayer(cfg.H, cfg.I, cfg.E_routed, cfg.top_k, cfg.act, cfg.quant,
+                    to_dev(W["w13"]), to_dev(W["w2"]), to_dev(W["w13_scale"]),
+                    to_dev(W["w2_scale"]), sc(a1), sc(a2), n_shared=cfg.n_shared,
+                    shared_gate=cfg.shared_gate, renormalize=cfg.renormalize)
+
+
+def weight_bytes_per_expert(cfg):
+    el = {"bf16": 2.0, "fp8_tensor": 1.0, "fp8_block": 1.0, "w4a8": 0.5}[cfg.quant]
+    w13 = cfg.N1 * cfg.H * el
+    w2 = cfg.H * cfg.I * el
+    if cfg.quant == "fp8_block":
+        w13 += (cfg.N1 // 128) * (cfg.H // 128) * 4
+        w2 += (cfg.H // 128) * (cfg.I // 128) * 4
+    elif cfg.quant == "w4a8":
+        w13 += cfg.N1 * (cfg.H // 128) * 2
+        w2 += cfg.H * (cfg.I // 128) * 2
+    elif cfg.quant == "fp8_tensor":
+        w13 += 4
+        w2 += 4
+    return w13, w2
+
+
+def algorithmic(cfg, M, ids):
+    """Bytes and FLOPs the pass must move / do, from the realised routing."""
+    import numpy as np
+    valid = ids[(ids >= 0) & (ids < cfg.E)]
+    touched = int(np.unique(valid).size)
+    A_v = int(valid.size)
+    w13, w2 = weight_bytes_per_expert(cfg)
+    a_el = 2 if cfg.quant == "bf16" else 1
+    x_b = M * cfg.H * 2
+    gemm1_bytes = touched * w13 + x_b + A_v * cfg.I * a_el
+    layer_bytes = (touched * (w13 + w2) + x_b + M * cfg.E_routed * 4
+                   + 2 * A_v * cfg.I * a_el + M * cfg.H * 2)
+    flops = 2.0 * A_v * cfg.H * cfg.N1 + 2.0 * A_v * cfg.I * cfg.H
+    gemm1_flops = 2.0 * A_v * cfg.H * cfg.N1
+    return dict(touched=touched, assignments=A_v, gemm1_bytes=gemm1_bytes,
+                layer_bytes=layer_bytes, flops=flops, gemm1_flops=gemm1_flops)
+
+
+class Pass:
+    """One layer pass through the component entry points on the current stream,
+    with events around each."""
+
+    def __init__(self, layer, x, logits, T):
+        self.layer, self.x, self.logits, self.T = layer, x, logits, T
+        self.b = layer.buffers(T)
+
+    def run(self, ev=None):
+        L, T, b = self.layer, self.T, self.b
+        if ev is not None:
+            ev[0].record()
+        L.route(T, self.logits, b)
+        L.align(T, b)
+        L.quant(T, self.x, b)
+        if ev is not None:
+            ev[1].record()
+        L.gemm1(T, self.x, b)
+        if ev is not None:
+            ev[2].record()
+        L.gemm2(T, b)
+        if ev is not None:
+            ev[3].record()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
+
+
+def cpu_baseline(cfg, W, tok, sc, min_seconds):
+    """The oracle as it stands, on the same workload's batch, repeated until at
+    least `min_seconds` of host time are spent."""
+    import numpy as np
+    import oracle
+    from synth.inputs import bf16_bits_to_f32
+    x = bf16_bits_to_f32(tok["x_bits"]).astype(np.float64)
+    M = x.shape[0]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.moe_forward(x, W["w13"], W["w2"], quant=cfg.quant, act=cfg.act,
+                           E_routed=cfg.E_routed, top_k=cfg.top_k,
+                           renormalize=cfg.renormalize, n_shared=cfg.n_shared,
+                           shared_gate=cfg.shared_gate, logits=tok["logits"],
+                           w13_scale=W["w13_scale"], w2_scale=W["w2_scale"],
+                           a1=sc["a1"], a2=sc["a2"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    return {"value": round(reps * M / el, 3), "unit": "tokens/s",
+            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"{reps} full pass(es) of the {M}-token batch ({cfg.name}), "
+                      f"fp64 NumPy, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the layer runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    cfg, M = workload(args.workload)
+    W = synth.make_weights(cfg)
+    tok = synth.make_tokens(cfg, M)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = make_layer(cfg, W, sc["a1"], sc["a2"])
+    x, lg = to_dev(tok["x_bits"]), to_dev(tok["logits"])
+    ps = Pass(layer, x, lg, M)
+
+    for _ in range(args.warmup):
+        ps.run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ps.run(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3      # us
+    g1 = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    g2 = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    span = evs[-1][3]
+    gpu_ms = evs[0][0].elapsed_time(span) / args.steps
+    ms = wall * 1e3 / args.steps
+
+    ids = ps.b["topk_ids"].cpu().numpy()
+    alg = algorithmic(cfg, M, ids)
+    achieved = alg["gemm1_bytes"] / (g1 * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(M / (ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.quant == "bf16" else ("fp8" if cfg.quant != "w4a8" else "int4xfp8"),
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} M={M}: hidden {cfg.H}, {cfg.E_routed} routed "
+                               f"+ {cfg.n_shared} shared experts, top-{cfg.top_k}, "
+                               f"intermediate {cfg.I}, {cfg.act}, {cfg.quant}",
+                   "tokens": M, "global_batch": M, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "gemm1_act", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(alg["gemm1_bytes"]),
+                     "avg_launch_us": round(float(g1), 2)},
+        "layer": {"gpu_ms_per_step": round(gpu_ms, 4), "us_route_align_quant": round(float(pre), 2),
+                  "us_gemm1": round(float(g1), 2), "us_gemm2_combine": round(float(g2), 2),
+                  "algorithmic_bytes": int(alg["layer_bytes"]),
+                  "hbm_frac": round(alg["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 3),
+                  "touched_experts": alg["touched"], "assignments": alg["assignments"]},
+    }
+    if not args.no_sweep:
+        out["sweep"] = sweep(cfg, W, layer)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, W, tok, sc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def sweep(cfg, W, layer):
+    """Each token count of the configuration: passes timed one at a time with
+    the caches evicted (a 512 MiB write) before each, outside the events."""
+    import numpy as np
+    import torch
+    import synth
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    res = []
+    for M in cfg.Ms:
+        tok = synth.make_tokens(cfg, M)
+        x, lg = to_dev(tok["x_bits"]), to_dev(tok["logits"])
+        ps = Pass(layer, x, lg, M)
+        for _ in range(3):
+            ps.run()
+        times = []
+        for _ in range(10):
+            flush.fill_(1.0)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            ps.run()
+            e.record()
+            e.synchronize()
+            times.append(s.elapsed_time(e) * 1e3)
+        us = float(np.median(times))
+        alg = algorithmic(cfg, M, ps.b["topk_ids"].cpu().numpy())
+        res.append({"M": M, "us_median": round(us, 2), "us_min": round(float(min(times)), 2),
+                    "tokens_per_s": round(M / (us * 1e-6), 1),
+                    "hbm_frac": round(alg["layer_bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "touched_experts": alg["touched"]})
+    del flush
+    return res
+
+
+if __name__ == "__main__":
+    main()

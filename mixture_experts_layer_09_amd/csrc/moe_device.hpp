@@ -1,0 +1,111 @@
+// Device helpers for the gfx950 kernels: vector types, MFMA wrappers, number
+// format conversions and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+// Weights are read once per pass: keep them from displacing reused lines.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// ---------------------------------------------------------------- MFMA
+// D[16x16] += A[16x32] * B[32x16] in bf16.  Lane l holds row (A) / column
+// (B) l % 16 and the 8 consecutive k at 8 * (l / 16); the result is
+// D[4 * (l / 16) + i][l % 16] in element i.
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D[16x16] += A[16x128] * B[128x16] in OCP e4m3 (unit block scales).  Lane l
+// holds row / column l % 16 and the 32 consecutive k at 32 * (l / 16).
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------- formats
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Four fp32 values -> four e4m3 codes (byte i from v[i]).  The hardware
+// conversion rounds to nearest even but turns magnitudes past the largest
+// finite value into NaN, so values are clamped to +-448 first.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return uint32_t(w);
+}
+
+// Signed int4 -> e4m3 codes, exact.  `nib` holds one nibble value (0..15,
+// two's complement) in the low 4 bits of each byte; the result holds the
+// e4m3 code of each.  Two byte-permute table lookups (values 0..7 and
+// -8..-1) and a per-byte select on the nibble's sign bit.
+__device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t nib) {
+  const uint32_t sel = nib & 0x07070707u;
+  // codes of 0,1,2,3 | 4,5,6,7
+  const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
+  // codes of -8,-7,-6,-5 | -4,-3,-2,-1
+  const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, sel);
+  const uint32_t m = ((nib >> 3) & 0x01010101u) * 0xFFu;
+  return (neg & m) | (pos & ~m);
+}
+
+// 16 bytes of packed int4 (32 values) -> 32 e4m3 codes.  Byte b of input
+// dword q holds value 8q + b in its low nibble and 8q + 4 + b in its high
+// nibble, so output dword 2q takes the low nibbles and 2q + 1 the high ones.
+__device__ __forceinline__ i32x8 int4x32_to_e4m3(const u32x4& v) {
+  i32x8 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r[2 * q] = int32_t(int4x4_to_e4m3(v[q] & 0x0F0F0F0Fu));
+    r[2 * q + 1] = int32_t(int4x4_to_e4m3((v[q] >> 4) & 0x0F0F0F0Fu));
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- math
+// SiLU from its definition, g * sigmoid(g), in fp32.
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace moe

@@ -1,0 +1,433 @@
+// Grouped expert GEMMs: GEMM1 with the activation in its epilogue, GEMM2 with
+// the routing weight, and the combine back into token order.
+//
+// GEMM1 (sglang PR 32944 page, sections 1-2; flashinfer PR 4329 page,
+// section 2): for each block of 16 aligned rows of expert e, h = W13[e] . x
+// over the gathered tokens; the packed W13 holds each group of 16 gate rows
+// next to its 16 up rows, so a wave computing a (gate, up) tile pair holds
+// gate channel c and up channel c in the same lane and register and applies
+// SiLU(gate) * up -- or relu(h)^2 for the non-gated layer (sglang PR 21321
+// page) -- before anything leaves registers; only the I activated columns are
+// stored, in the compute format.
+// GEMM2 (flashinfer PR 4329 page, sections 3-4): y = W2[e] . a, scaled by the
+// routing weight, written per assignment in fp32; the combine then sums each
+// token's K' rows in slot order and rounds once to bf16.
+//
+// MFMA operands: the weights are the A operand (16 weight rows per tile) and
+// the tokens the B operand (16 tokens per tile), so a block with a handful of
+// tokens still streams whole weight rows through the matrix cores.  Weights
+// come straight from HBM into registers in 16-byte lane loads of pre-tiled
+// fragments (1 or 2 KiB per wave load); several k-steps of fragments are in
+// flight per wave.
+#include "moe_device.hpp"
+#include "moe_launch.hpp"
+
+namespace moe {
+
+namespace {
+
+struct GemmArgs {
+  const uint8_t* b;          // B rows: GEMM1 x [T][K], GEMM2 a2 [rows][K]
+  const float* b_scale;      // FP8_BLOCK: per B row per 128 K
+  const uint8_t* w;          // packed weights
+  const float* w_scale;      // packed scales
+  const float* a1;           // static x scale (FP8_TENSOR, W4A8)
+  const float* a2;           // static intermediate scale (FP8_TENSOR, W4A8)
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  const float* topk_w;       // GEMM2
+  uint8_t* out;              // GEMM1: a2 [rows][I]; GEMM2: y fp32 [A][H]
+  float* out_scale;          // GEMM1 FP8_BLOCK: [rows][I/128]
+  int K, N, I, H, Kp, A, steps, tiles;
+};
+
+template <int Q> struct QT;
+template <> struct QT<MOE_QUANT_BF16> {
+  static constexpr int AV = 1, BV = 1, FRAG = 1024, KSTEP = 32, EB = 2;
+};
+template <> struct QT<MOE_QUANT_FP8_TENSOR> {
+  static constexpr int AV = 2, BV = 2, FRAG = 2048, KSTEP = 128, EB = 1;
+};
+template <> struct QT<MOE_QUANT_FP8_BLOCK> {
+  static constexpr int AV = 2, BV = 2, FRAG = 2048, KSTEP = 128, EB = 1;
+};
+template <> struct QT<MOE_QUANT_W4A8> {
+  static constexpr int AV = 1, BV = 2, FRAG = 1024, KSTEP = 128, EB = 1;
+};
+
+template <int Q, int WT>
+struct Stage {
+  u32x4 a[WT][QT<Q>::AV];
+  u32x4 b[QT<Q>::BV];
+  float bs;        // FP8_BLOCK: B row scale of this k-block
+  float ws[WT];    // FP8_BLOCK: weight block scale per tile
+  f32x4 ws4[WT];   // W4A8: group scales of the lane's 4 rows per tile
+};
+
+template <int Q>
+__device__ __forceinline__ i32x8 fp8_pair(const u32x4& lo, const u32x4& hi) {
+  i32x8 r;
+  r[0] = int(lo[0]); r[1] = int(lo[1]); r[2] = int(lo[2]); r[3] = int(lo[3]);
+  r[4] = int(hi[0]); r[5] = int(hi[1]); r[6] = int(hi[2]); r[7] = int(hi[3]);
+  return r;
+}
+
+// Weight row block (128 rows, checkpoint order) of a packed W13 row tile.
+__device__ __forceinline__ int w13_row_block(int tile, int I, bool gated) {
+  if (!gated) return tile / 8;
+  const int pair = tile >> 1, half = tile & 1;
+  return (half * I + pair * 16) / 128;
+}
+
+}  // namespace
+
+template <int PHASE, int Q, int ACT, int WT, int KS>
+__global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
+  using T = QT<Q>;
+  constexpr int RG = 4 / KS;       // waves along the weight rows
+  constexpr int TPW = RG * WT;     // row tiles per workgroup
+  constexpr int D = Q == MOE_QUANT_BF16 ? 4 : 2;  // k-steps loaded ahead
+  constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rg = wave % RG, kp = wave / RG;
+  const int blk = blockIdx.y;
+  if (blk * 16 >= *g.num_padded) return;  // uniform: past the last real block
+  const int e = g.block_expert[blk];
+  const int tile0 = blockIdx.x * TPW + rg * WT;
+  const bool active = tile0 < g.tiles;
+  const int grp = lane >> 4;            // k-run of the lane
+  const int m = blk * 16 + (lane & 15); // padded row = B column of the lane
+  const int f = g.sorted_ids[m];
+
+  // B row of the lane: GEMM1 gathers the token, GEMM2 reads the padded row.
+  int brow;
+  if (PHASE == 1) brow = f < g.A ? f / g.Kp : 0;
+  else brow = m;
+  const uint8_t* bp = g.b + (size_t(brow) * g.K + grp * (T::KSTEP / 4)) * T::EB;
+  const size_t ebytes = size_t(g.tiles) * g.steps * T::FRAG;
+  const uint8_t* wp = g.w + size_t(e) * ebytes + size_t(tile0) * g.steps * T::FRAG + lane * 16;
+  const int kblocks = g.K / 128;
+
+  const int per = (g.steps + KS - 1) / KS;
+  const int s0 = min(g.steps, kp * per), s1 = min(g.steps, s0 + per);
+
+  f32x4 acc[WT];
+#pragma unroll
+  for (int j = 0; j < WT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](Stage<Q, WT>& S, int s) {
+#pragma unroll
+    for (int j = 0; j < WT; ++j) {
+      const uint8_t* p = wp + (size_t(j) * g.steps + s) * T::FRAG;
+#pragma unroll
+      for (int v = 0; v < T::AV; ++v) S.a[j][v] = ld16_stream(p + v * 1024);
+    }
+    const uint8_t* q = bp + size_t(s) * T::KSTEP * T::EB;
+#pragma unroll
+    for (int v = 0; v < T::BV; ++v) S.b[v] = ld16(q + v * 16);
+    if (Q == MOE_QUANT_FP8_BLOCK) {
+      S.bs = g.b_scale[size_t(brow) * kblocks + s];
+#pragma unroll
+      for (int j = 0; j < WT; ++j) {
+        const int rb = PHASE == 1 ? w13_row_block(tile0 + j, g.I, GATED) : (tile0 + j) / 8;
+        S.ws[j] = g.w_scale[(size_t(e) * (g.N / 128) + rb) * kblocks + s];
+      }
+    }
+    if (Q == MOE_QUANT_W4A8) {
+#pragma unroll
+      for (int j = 0; j < WT; ++j)
+        S.ws4[j] = *reinterpret_cast<const f32x4*>(
+            g.w_scale + ((size_t(e) * g.tiles + tile0 + j) * g.steps + s) * 16 + grp * 4);
+    }
+  };
+
+  auto compute = [&](const Stage<Q, WT>& S) {
+    if (Q == MOE_QUANT_BF16) {
+#pragma unroll
+      for (int j = 0; j < WT; ++j) acc[j] = mfma_bf16(S.a[j][0], S.b[0], acc[j]);
+    } else {
+      const i32x8 bb = fp8_pair<Q>(S.b[0], S.b[1]);
+#pragma unroll
+      for (int j = 0; j < WT; ++j) {
+        if (Q == MOE_QUANT_FP8_TENSOR) {
+          acc[j] = mfma_fp8(fp8_pair<Q>(S.a[j][0], S.a[j][1]), bb, acc[j]);
+        } else if (Q == MOE_QUANT_FP8_BLOCK) {
+          const f32x4 p = mfma_fp8(fp8_pair<Q>(S.a[j][0], S.a[j][1]), bb, f32x4{0.f, 0.f, 0.f, 0.f});
+          const float sc = S.bs * S.ws[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(p[i], sc, acc[j][i]);
+        } else {
+          const f32x4 p = mfma_fp8(int4x32_to_e4m3(S.a[j][0]), bb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(p[i], S.ws4[j][i], acc[j][i]);
+        }
+      }
+    }
+  };
+
+  if (active) {
+    Stage<Q, WT> st[D];
+    const int n = s1 - s0;
+    const int G = n / D;
+    if (G > 0) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) load(st[d], s0 + d);
+      for (int gi = 0; gi < G - 1; ++gi) {
+        const int sn = s0 + (gi + 1) * D;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          compute(st[d]);
+          load(st[d], sn + d);
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < D; ++d) compute(st[d]);
+    }
+    for (int s = s0 + G * D; s < s1; ++s) {
+      load(st[0], s);
+      compute(st[0]);
+    }
+  }
+
+  // ---- K-split: the partial sums of waves kp > 0 join wave kp == 0
+  if (KS > 1) {
+    __shared__ f32x4 red[(KS > 1 ? KS - 1 : 1) * RG * WT * 64];
+    if (kp > 0) {
+#pragma unroll
+      for (int j = 0; j < WT; ++j) red[(((kp - 1) * RG + rg) * WT + j) * 64 + lane] = acc[j];
+    }
+    __syncthreads();
+    if (kp == 0) {
+      for (int k = 1; k < KS; ++k) {
+#pragma unroll
+        for (int j = 0; j < WT; ++j) {
+          const f32x4 o = red[(((k - 1) * RG + rg) * WT + j) * 64 + lane];
+          acc[j] += o;
+        }
+      }
+    }
+    if (kp > 0) return;
+  }
+
+  if (PHASE == 1) {
+    // ---- GEMM1 epilogue: dequantise, activate, store the half-width row
+    float alpha = 1.f;
+    if (Q == MOE_QUANT_FP8_TENSOR) alpha = g.w_scale[e] * *g.a1;
+    if (Q == MOE_QUANT_W4A8) alpha = *g.a1;
+    constexpr int NV = GATED ? WT / 2 : WT;  // 4-channel vectors per lane
+    float a[NV][4];
+    int cbase[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (GATED) {
+          const float gt = alpha * acc[2 * v][i], up = alpha * acc[2 * v + 1][i];
+          a[v][i] = silu(gt) * up;
+        } else {
+          const float h = fmaxf(alpha * acc[v][i], 0.f);
+          a[v][i] = h * h;
+        }
+      }
+      cbase[v] = (GATED ? (tile0 / 2 + v) : (tile0 + v)) * 16 + grp * 4;
+    }
+    if (Q == MOE_QUANT_BF16) {
+      if (active) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          u32x2 o;
+          o[0] = bf16_bits(a[v][0]) | (bf16_bits(a[v][1]) << 16);
+          o[1] = bf16_bits(a[v][2]) | (bf16_bits(a[v][3]) << 16);
+          *reinterpret_cast<u32x2*>(g.out + (size_t(m) * g.I + cbase[v]) * 2) = o;
+        }
+      }
+    } else if (Q == MOE_QUANT_FP8_BLOCK) {
+      // per token and 128 channels: s = amax / 448, q = e4m3(a / s)
+      __shared__ float amax_s[4][16];
+      constexpr int CH = NV * 16;  // channels per wave
+      constexpr int WPG = 128 / CH;  // waves per 128-channel group
+      float am = 0.f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(a[v][i]));
+      am = fmaxf(am, __shfl_xor(am, 16, 64));
+      am = fmaxf(am, __shfl_xor(am, 32, 64));
+      if (grp == 0) amax_s[wave][lane & 15] = active ? am : 0.f;
+      __syncthreads();
+      const int w0 = wave - wave % WPG;
+      float gm = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPG; ++w) gm = fmaxf(gm, amax_s[w0 + w][lane & 15]);
+      const float s = gm > 0.f ? gm / 448.f : 1.f;
+      if (active) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const uint32_t q = e4m3x4(a[v][0] / s, a[v][1] / s, a[v][2] / s, a[v][3] / s);
+          *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) = q;
+        }
+        if (grp == 0 && wave == w0) g.out_scale[size_t(m) * (g.I / 128) + cbase[0] / 128] = s;
+      }
+    } else {
+      if (active) {
+        const float s2 = *g.a2;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const uint32_t q = e4m3x4(a[v][0] / s2, a[v][1] / s2, a[v][2] / s2, a[v][3] / s2);
+          *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) = q;
+        }
+      }
+    }
+  } else {
+    // ---- GEMM2 epilogue: dequantise, weight, write the assignment's row
+    if (!active || f >= g.A) return;
+    float alpha = 1.f;
+    if (Q == MOE_QUANT_FP8_TENSOR) alpha = g.w_scale[e] * *g.a2;
+    if (Q == MOE_QUANT_W4A8) alpha = *g.a2;
+    const float wgt = alpha * g.topk_w[f];
+#pragma unroll
+    for (int j = 0; j < WT; ++j) {
+      const int n = (tile0 + j) * 16 + grp * 4;
+      *reinterpret_cast<f32x4*>(g.out + (size_t(f) * g.H + n) * 4) = acc[j] * wgt;
+    }
+  }
+}
+
+// out[t][:] = bf16(sum over valid slots j of y[t*K' + j][:]) with y in fp32,
+// one thread per 8 hidden values.
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
+                                                     const float* __restrict__ y,
+                                                     uint16_t* __restrict__ out, int T, int H,
+                                                     int Kp, int E) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int h8 = H / 8;
+  if (i >= int64_t(T) * h8) return;
+  const int t = int(i / h8), c = int(i % h8) * 8;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < Kp; ++j) {
+    const int e = ids[size_t(t) * Kp + j];
+    if (e < 0 || e >= E) continue;
+    const float* row = y + (size_t(t) * Kp + j) * H + c;
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(row);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(row + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s[k] += v0[k];
+      s[4 + k] += v1[k];
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = bf16_bits(s[2 * k]) | (bf16_bits(s[2 * k + 1]) << 16);
+  *reinterpret_cast<u32x4*>(out + size_t(t) * H + c) = o;
+}
+
+namespace {
+
+template <int PHASE, int Q, int ACT>
+hipError_t dispatch_stream(const GemmCfg& c, dim3 grid, const GemmArgs& a, hipStream_t st) {
+  const dim3 block(256);
+  if constexpr (PHASE == 1 && Q == MOE_QUANT_FP8_BLOCK) {
+    // the per-128-channel amax needs the whole workgroup on one row range
+    if (c.wt == 4 && c.ksplit == 1) gemm_stream<PHASE, Q, ACT, 4, 1><<<grid, block, 0, st>>>(a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (c.wt == 4 && c.ksplit == 1) gemm_stream<PHASE, Q, ACT, 4, 1><<<grid, block, 0, st>>>(a);
+    else if (c.wt == 4 && c.ksplit == 2) gemm_stream<PHASE, Q, ACT, 4, 2><<<grid, block, 0, st>>>(a);
+    else if (c.wt == 4 && c.ksplit == 4) gemm_stream<PHASE, Q, ACT, 4, 4><<<grid, block, 0, st>>>(a);
+    else if (c.wt == 2 && c.ksplit == 4) gemm_stream<PHASE, Q, ACT, 2, 4><<<grid, block, 0, st>>>(a);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int PHASE, int ACT>
+hipError_t dispatch_quant(int quant, const GemmCfg& c, dim3 grid, const GemmArgs& a,
+                          hipStream_t st) {
+  switch (quant) {
+    case MOE_QUANT_BF16: return dispatch_stream<PHASE, MOE_QUANT_BF16, ACT>(c, grid, a, st);
+    case MOE_QUANT_FP8_TENSOR: return dispatch_stream<PHASE, MOE_QUANT_FP8_TENSOR, ACT>(c, grid, a, st);
+    case MOE_QUANT_FP8_BLOCK: return dispatch_stream<PHASE, MOE_QUANT_FP8_BLOCK, ACT>(c, grid, a, st);
+    case MOE_QUANT_W4A8: return dispatch_stream<PHASE, MOE_QUANT_W4A8, ACT>(c, grid, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+dim3 stream_grid(const GemmCfg& c, int tiles, int64_t blocks) {
+  const int tpw = (4 / c.ksplit) * c.wt;
+  return dim3(unsigned((tiles + tpw - 1) / tpw), unsigned(blocks));
+}
+
+}  // namespace
+
+hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, const float* xs,
+                        const moe_weights& w, const int32_t* sorted_ids,
+                        const int32_t* block_expert, const int32_t* num_padded, void* a2,
+                        float* a2s, hipStream_t stream) {
+  if (q.max_blocks == 0) return hipSuccess;
+  GemmArgs a{};
+  a.b = static_cast<const uint8_t*>(x);
+  a.b_scale = xs;
+  a.w = static_cast<const uint8_t*>(w.w13);
+  a.w_scale = w.w13_scale;
+  a.a1 = w.a1_scale;
+  a.a2 = w.a2_scale;
+  a.sorted_ids = sorted_ids;
+  a.block_expert = block_expert;
+  a.num_padded = num_padded;
+  a.out = static_cast<uint8_t*>(a2);
+  a.out_scale = a2s;
+  a.K = p.H;
+  a.N = q.N1;
+  a.I = p.I;
+  a.H = p.H;
+  a.Kp = q.Kp;
+  a.A = int(q.A);
+  a.steps = q.ksteps_h;
+  a.tiles = q.N1 / 16;
+  const dim3 grid = stream_grid(q.g1, a.tiles, q.max_blocks);
+  if (q.gated) return dispatch_quant<1, MOE_ACT_SILU_GATED>(p.quant, q.g1, grid, a, stream);
+  return dispatch_quant<1, MOE_ACT_RELU2>(p.quant, q.g1, grid, a, stream);
+}
+
+hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, const float* a2s,
+                        const moe_weights& w, const int32_t* sorted_ids,
+                        const int32_t* block_expert, const int32_t* num_padded,
+                        const float* topk_w, float* y, hipStream_t stream) {
+  if (q.max_blocks == 0) return hipSuccess;
+  GemmArgs a{};
+  a.b = static_cast<const uint8_t*>(a2);
+  a.b_scale = a2s;
+  a.w = static_cast<const uint8_t*>(w.w2);
+  a.w_scale = w.w2_scale;
+  a.a1 = w.a1_scale;
+  a.a2 = w.a2_scale;
+  a.sorted_ids = sorted_ids;
+  a.block_expert = block_expert;
+  a.num_padded = num_padded;
+  a.topk_w = topk_w;
+  a.out = reinterpret_cast<uint8_t*>(y);
+  a.K = p.I;
+  a.N = p.H;
+  a.I = p.I;
+  a.H = p.H;
+  a.Kp = q.Kp;
+  a.A = int(q.A);
+  a.steps = q.ksteps_i;
+  a.tiles = p.H / 16;
+  const dim3 grid = stream_grid(q.g2, a.tiles, q.max_blocks);
+  return dispatch_quant<2, 0>(p.quant, q.g2, grid, a, stream);
+}
+
+hipError_t launch_combine(const moe_problem& p, const Plan& q, const int32_t* topk_ids,
+                          const float* y, uint16_t* out, hipStream_t stream) {
+  const int64_t n = int64_t(p.T) * (p.H / 8);
+  if (n == 0) return hipSuccess;
+  combine_kernel<<<unsigned((n + 255) / 256), 256, 0, stream>>>(topk_ids, y, out, p.T, p.H, q.Kp,
+                                                                p.E);
+  return hipGetLastError();
+}
+
+}  // namespace moe

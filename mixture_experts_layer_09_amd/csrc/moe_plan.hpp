@@ -1,0 +1,64 @@
+// Host-side planning for one layer call: validation, the tile table, buffer
+// capacities and the workspace layout.  Pure C++ (no HIP), so it builds and is
+// tested without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kGroup = 128;        // block / group width of the quantised formats
+constexpr int kAlignChunk = 1024;  // assignments per workgroup in the align kernels
+constexpr int kMaxRouted = 1024;   // logits per token the routing kernel holds
+constexpr int kMaxSlots = 64;      // K' = top_k + n_shared limit (one lane each)
+
+// Which GEMM kernel runs and how it is tiled.
+//  kind 0: weight-streaming kernel, one 16-row block of tokens per workgroup,
+//          A (weights) and B (tokens) fragments loaded straight into registers;
+//  kind 1: tiled kernel, BM tokens staged through LDS and shared by the waves.
+struct GemmCfg {
+  int kind;    // 0 stream, 1 tiled
+  int nt;      // 16-token MFMA tiles per block (BM = 16 * nt)
+  int wt;      // 16-row weight tiles per wave
+  int ksplit;  // waves of a workgroup that split K (stream kernel)
+  int waves;   // waves per workgroup
+};
+
+struct Plan {
+  int32_t Kp = 0;          // slots per token
+  int64_t A = 0;           // assignments T * Kp
+  int32_t BM = 0;          // resolved block_m
+  int64_t max_blocks = 0;
+  int64_t max_rows = 0;
+  int32_t chunks = 0;      // align chunks of kAlignChunk assignments
+  bool gated = false;
+  int32_t N1 = 0;          // rows of W13 (2I or I)
+  int32_t ksteps_h = 0;    // MFMA k-steps along H
+  int32_t ksteps_i = 0;    // MFMA k-steps along I
+  int32_t kstep = 0;       // K elements per MFMA k-step (32 bf16, 128 fp8/int4)
+  int32_t a2_elem = 0;     // bytes per intermediate element
+  GemmCfg g1{}, g2{};
+  // moe_forward workspace layout (byte offsets, 256-B aligned)
+  size_t off_ids = 0, off_w = 0, off_sorted = 0, off_bexp = 0, off_offsets = 0,
+         off_npad = 0, off_align = 0, off_xq = 0, off_xs = 0, off_a2 = 0,
+         off_a2s = 0, off_y = 0, ws_total = 0;
+  size_t align_ws = 0, combine_ws = 0;
+};
+
+// Records a failure detail for moe_last_error() and returns `status`.
+int fail(int status, const std::string& msg);
+void clear_error();
+const char* last_error();
+
+// Validates `p` and fills `plan`.  Returns MOE_OK or an error status.
+int make_plan(const moe_problem* p, Plan* plan);
+
+int32_t padded_intermediate(int32_t I, int32_t act, int32_t quant);
+size_t packed_weight_bytes(const moe_problem& p, int which);
+size_t packed_scale_bytes(const moe_problem& p, int which);
+
+}  // namespace moe

@@ -1,0 +1,131 @@
+"""The C ABI boundary, on the CPU (no kernel is launched).
+
+* libmoe.so loads and exports every entry point include/moe.h declares;
+* the host-only planner library (built with g++, no HIP) returns each
+  validation status for the argument errors it guards against, and the
+  capacity / workspace formulas hold.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_09_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_matches_binding():
+    assert _declared() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+@pytest.fixture(scope="module")
+def plan():
+    return moe.load_plan_lib()
+
+
+def P(**kw):
+    base = dict(T=8, H=256, I=512, E_routed=8, top_k=2)
+    base.update(kw)
+    return moe.problem(**base)
+
+
+def _st(lib, p):
+    return lib.moe_validate(ctypes.byref(p))
+
+
+def test_valid_problems(plan):
+    for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8"):
+        for a in ("silu", "relu2"):
+            assert _st(plan, P(quant=q, act=a)) == moe.MOE_OK
+    assert _st(plan, P(T=0)) == moe.MOE_OK
+    assert _st(plan, P(n_shared=1, E_routed=8)) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(H=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(I=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(act=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(quant=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(block_m=17), moe.MOE_ERR_INVALID_ARG),
+    (dict(H=200), moe.MOE_ERR_ALIGNMENT),
+    (dict(I=500), moe.MOE_ERR_ALIGNMENT),                       # gated bf16 needs 32
+    (dict(I=96, act="relu2"), moe.MOE_ERR_ALIGNMENT),           # non-gated needs 128
+    (dict(I=160, quant="fp8_tensor"), moe.MOE_ERR_ALIGNMENT),   # fp8 needs 128
+    (dict(E_routed=1100, top_k=2), moe.MOE_ERR_UNSUPPORTED),    # > 1024 slots
+    (dict(E_routed=100, top_k=65), moe.MOE_ERR_UNSUPPORTED),    # K' > 64
+    (dict(T=1 << 20, H=4096, top_k=8), moe.MOE_ERR_UNSUPPORTED),  # int32 offsets
+])
+def test_validation_errors(plan, kw, status):
+    assert _st(plan, P(**kw)) == status
+    assert plan.moe_last_error()  # a detail string is recorded
+
+
+def test_inconsistent_slots(plan):
+    p = P()
+    p.E = 9  # E != E_routed + n_shared
+    assert _st(plan, p) == moe.MOE_ERR_INVALID_ARG
+    p = P(renormalize=True)
+    p.renormalize = 3
+    assert _st(plan, p) == moe.MOE_ERR_INVALID_ARG
+    p = P()
+    p.shared_gate = float("inf")
+    assert _st(plan, p) == moe.MOE_ERR_INVALID_ARG
+    assert plan.moe_validate(None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_padded_intermediate(plan):
+    f = plan.moe_padded_intermediate
+    assert f(768, 0, 0) == 768 and f(1000, 0, 0) == 1024 and f(17, 0, 0) == 32
+    assert f(2688, 1, 1) == 2688 and f(2600, 1, 0) == 2688 and f(100, 0, 2) == 128
+    assert f(0, 0, 0) == moe.MOE_ERR_INVALID_ARG and f(10, 3, 0) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("T,K,E", [(1, 8, 128), (64, 8, 128), (16, 11, 513), (4096, 11, 513),
+                                   (8192, 8, 20), (3, 2, 8)])
+def test_capacity_bounds(plan, T, K, E):
+    p = P(T=T, E_routed=E, top_k=K, H=2048, I=768)
+    bm = plan.moe_block_m(ctypes.byref(p))
+    A = T * K
+    nb = plan.moe_max_blocks(ctypes.byref(p))
+    # no expert can hold more blocks than ceil(count / BM); summed over at
+    # most min(E, A) non-empty experts
+    assert nb == min(A, (A + min(E, A) * (bm - 1)) // bm)
+    assert plan.moe_max_padded_rows(ctypes.byref(p)) == nb * bm
+    ws = plan.moe_workspace_bytes(ctypes.byref(p))
+    assert ws >= A * 2048 * 4 + nb * bm * 768 * 2  # fp32 y rows + intermediate at least
+
+
+def test_packed_bytes(plan):
+    w, s = ctypes.c_size_t(), ctypes.c_size_t()
+    cases = [("bf16", "silu", 8 * 1024 * 256 * 2, 0), ("fp8_tensor", "relu2", 8 * 512 * 256, 32),
+             ("fp8_block", "silu", 8 * 1024 * 256, 8 * 8 * 2 * 4),
+             ("w4a8", "silu", 8 * 1024 * 256 // 2, 8 * 1024 * 2 * 4)]
+    for q, a, wb, sb in cases:
+        p = P(quant=q, act=a)
+        assert plan.moe_packed_bytes(ctypes.byref(p), 13, ctypes.byref(w), ctypes.byref(s)) == 0
+        assert (w.value, s.value) == (wb, sb)
+    assert plan.moe_packed_bytes(ctypes.byref(P()), 5, ctypes.byref(w), ctypes.byref(s)) \
+        == moe.MOE_ERR_INVALID_ARG
+
+
+def test_status_strings(plan):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert plan.moe_status_string(st).decode().startswith("MOE_")

@@ -1,0 +1,171 @@
+"""GPU parity of the whole layer (moe_forward through the C ABI) vs the oracle.
+
+All five configurations at every token count they name.  The decode-sized
+and tiny passes are compared on every output; the full-size prefill passes
+(cfg3 M=4096, cfg4 M=128/8192, cfg5 M=8192, cfg3 M=256) run the whole pass on
+the GPU and compare a seeded sample of token rows (first and last included)
+with the oracle on those tokens.  Tolerances: max-abs 2e-2 and rel-L2 1e-2
+(bf16, fp8), rel-L2 3e-2 (int4 weights).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_09_amd as moe
+import oracle
+import synth
+from gpu_cases import (ad_hoc, assert_close, build_layer, dev, oracle_forward, say,
+                       scalar, weights_for)
+
+pytestmark = pytest.mark.gpu
+
+# (cid, M, sampled token rows or None for all)
+FULL = [(1, 64, None), (2, 1, None), (2, 8, None), (2, 32, None), (2, 64, None),
+        (3, 16, None), (3, 256, 24), (3, 4096, 12), (4, 1, None), (4, 128, 12),
+        (4, 8192, 6), (5, 8192, 8)]
+
+
+def _sample(M, n, seed):
+    if n is None or n >= M:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, M - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], mid]))
+
+
+@pytest.mark.parametrize("cid,M,n", FULL, ids=[f"cfg{c}-M{m}" for c, m, _ in FULL])
+def test_forward_config(cid, M, n):
+    cfg = synth.CONFIGS[cid]
+    say(f"forward {cfg.name} M={M} sample={n}")
+    W = weights_for(cfg)
+    tok = synth.make_tokens(cfg, M)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
+    out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    rows = _sample(M, n, 1000 * cid + M)
+    ref = oracle_forward(cfg, W, tok["x_bits"][rows], tok["logits"][rows], sc["a1"], sc["a2"])
+    assert_close(got[rows], ref["out"], cfg.quant, f"{cfg.name} M={M}")
+    del layer
+    torch.cuda.empty_cache()
+
+
+SMALL = [(q, a) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8") for a in ("silu", "relu2")]
+
+
+@pytest.mark.parametrize("quant,act", SMALL)
+@pytest.mark.parametrize("T", [1, 37])
+def test_forward_small_ragged(quant, act, T):
+    """Several row tiles with a partly filled last workgroup, an odd number
+    of k-steps and token counts that leave ragged blocks."""
+    I = 160 if quant == "bf16" else 384
+    if act == "relu2" and quant == "bf16":
+        I = 384
+    cfg = ad_hoc(90, quant, act, H=384, I=I, E_routed=10, top_k=3, n_shared=1)
+    say(f"small {quant} {act} T={T} I={I}")
+    W = synth.make_weights(cfg, seed=4242)
+    tok = synth.make_tokens(cfg, T, seed=77 + T)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
+    out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
+    torch.cuda.synchronize()
+    ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"], sc["a1"], sc["a2"])
+    assert_close(out.float().cpu().numpy(), ref["out"], quant, f"small {quant} {act} T={T}")
+
+
+def test_components_equal_forward():
+    """The separate entry points produce exactly moe_forward's output."""
+    cfg = synth.CONFIGS[2]
+    W = weights_for(cfg)
+    tok = synth.make_tokens(cfg, 8)
+    layer = build_layer(cfg, W)
+    x, lg = dev(tok["x_bits"]), dev(tok["logits"])
+    out = layer.forward(x, lg)
+    b = layer.buffers(8)
+    layer.route(8, lg, b)
+    layer.align(8, b)
+    layer.quant(8, x, b)
+    layer.gemm1(8, x, b)
+    layer.gemm2(8, b)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), b["out"].view(torch.int16))
+
+
+@pytest.mark.parametrize("quant", ["bf16", "fp8_block"])
+def test_prerouted_with_masked_slots(quant):
+    """Routing supplied by the caller; ids outside [0, E) contribute nothing."""
+    cfg = ad_hoc(91, quant, "silu", H=256, I=256, E_routed=12, top_k=4)
+    W = synth.make_weights(cfg, seed=99)
+    T = 29
+    tok = synth.make_tokens(cfg, T, seed=5)
+    rng = np.random.default_rng(6)
+    ids = rng.integers(0, 12, (T, 4)).astype(np.int32)
+    ids[rng.random((T, 4)) < 0.25] = -1
+    ids[3] = -1                                   # a token with no valid slot
+    w = rng.uniform(0.1, 1.0, (T, 4)).astype(np.float32)
+    layer = build_layer(cfg, W)
+    out = layer.forward(dev(tok["x_bits"]), None, dev(ids), dev(w))
+    torch.cuda.synchronize()
+    ref = oracle_forward(cfg, W, tok["x_bits"], topk_ids=ids, topk_w=w.astype(np.float64))
+    got = out.float().cpu().numpy()
+    assert np.all(got[3] == 0.0)
+    assert_close(got, ref["out"], quant, "prerouted")
+
+
+def test_pack_swap_and_padding():
+    """[Up, Gate] checkpoints with the swap flag, and an unaligned I padded
+    with zeros at pack time, give the unpadded gate-first result."""
+    src_I, I = 200, moe.padded_intermediate(200, "silu", "bf16")
+    assert I == 224
+    cfg = ad_hoc(92, "bf16", "silu", H=256, I=src_I, E_routed=6, top_k=2)
+    W = synth.make_weights(cfg, seed=12)
+    up_first = np.concatenate([W["w13"][:, src_I:], W["w13"][:, :src_I]], axis=1)
+    T = 21
+    tok = synth.make_tokens(cfg, T, seed=13)
+    from mixture_experts_layer_09_amd.layer import MoELayer
+    layer = MoELayer(256, I, 6, 2, "silu", "bf16", dev(up_first), dev(W["w2"]), src_I=src_I,
+                     swap_halves=True)
+    out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
+    torch.cuda.synchronize()
+    ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"])
+    assert_close(out.float().cpu().numpy(), ref["out"], "bf16", "swap+pad")
+
+
+def test_zero_tokens_is_a_noop():
+    cfg = synth.CONFIGS[1]
+    W = weights_for(cfg)
+    layer = build_layer(cfg, W)
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((0, cfg.E_routed), dtype=torch.float32, device="cuda")
+    out = layer.forward(x, lg)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.H)
+
+
+def test_token_permutation_equivariant_on_gpu():
+    cfg = synth.CONFIGS[1]
+    W = weights_for(cfg)
+    tok = synth.make_tokens(cfg, 64)
+    layer = build_layer(cfg, W)
+    perm = np.random.default_rng(3).permutation(64)
+    a = layer.forward(dev(tok["x_bits"]), dev(tok["logits"])).float().cpu().numpy()
+    b = layer.forward(dev(tok["x_bits"][perm]), dev(tok["logits"][perm])).float().cpu().numpy()
+    # each token's row is computed by the same kernels in the same order
+    assert np.array_equal(a[perm], b)
+
+
+def test_invalid_call_enqueues_nothing():
+    cfg = synth.CONFIGS[1]
+    W = weights_for(cfg)
+    layer = build_layer(cfg, W)
+    p = layer.problem(4)
+    out = torch.zeros((4, cfg.H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")     # far too small
+    x = torch.zeros((4, cfg.H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.zeros((4, cfg.E_routed), dtype=torch.float32, device="cuda")
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward(p, layer.w, x, lg, None, None, out, ws)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out.float()) == 0
