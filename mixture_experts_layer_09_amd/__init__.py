@@ -90,11 +90,29 @@ def _declare(lib, host_only=False):
     return lib
 
 
+def _hip_runtimes():
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m mixture_experts_layer_09_amd.build`")
-    return _declare(ctypes.CDLL(LIB_PATH))
+    # torch ships its own HIP runtime.  Loading it first makes libmoe.so bind to
+    # that same runtime (same soname) instead of mapping a second one, so that
+    # torch's device memory and streams and the library's kernels live in one
+    # runtime.
+    import torch  # noqa: F401
+    lib = _declare(ctypes.CDLL(LIB_PATH))
+    rts = _hip_runtimes()
+    if len(rts) > 1:
+        raise ImportError("two HIP runtimes are mapped into this process: " + ", ".join(rts))
+    return lib
 
 
 lib = _load()

@@ -129,3 +129,8 @@ def test_packed_bytes(plan):
 def test_status_strings(plan):
     for st in (0, -1, -2, -3, -4, -5):
         assert plan.moe_status_string(st).decode().startswith("MOE_")
+
+
+def test_single_hip_runtime():
+    """The library binds to the HIP runtime torch brought into the process."""
+    assert len(moe._hip_runtimes()) == 1
