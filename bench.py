@@ -3,7 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload cfg2_M64] [--gpus 1]
 
-One step is one whole pass of the layer -- route, align, (fp8 quantise),
+One step is one whole pass of the layer -- route + (fp8 quantise) + align,
 GEMM1 + activation, GEMM2 + combine -- over one batch of synthetic tokens
 already resident in HBM, issued as the C-ABI entry points on the current HIP
 stream (the same sequence moe_forward runs).  The default workload is the
@@ -124,9 +124,7 @@ class Pass:
         L, T, b = self.layer, self.T, self.b
         if ev is not None:
             ev[0].record()
-        L.route(T, self.logits, b)
-        L.align(T, b)
-        L.quant(T, self.x, b)
+        L.prepare(T, self.logits, self.x, b)
         if ev is not None:
             ev[1].record()
         L.gemm1(T, self.x, b)

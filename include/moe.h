@@ -228,6 +228,17 @@ int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* sorted_ids
               int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
               void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* Everything before GEMM1 in one call: moe_route (when logits is not NULL;
+ * otherwise topk_ids is the caller's routing, an input), moe_quant_act (when
+ * x is not NULL and the mode is fp8 / W4A8; a1_scale, xq, x_scale as there)
+ * and moe_align, with the arguments of those entry points.  Decode-sized
+ * batches (T <= 128, T*K' <= 1024) run as one kernel launch, larger ones as
+ * the separate kernels.  Outputs are bit-identical to the separate calls. */
+int moe_prepare(const moe_problem* p, const float* logits, int32_t* topk_ids, float* topk_w,
+                const uint16_t* x, const float* a1_scale, uint8_t* xq, float* x_scale,
+                int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                int32_t* num_padded, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* fp8 activation quantisation of x (bf16 [T][H]) for the fp8 and W4A8 modes:
  *   FP8_TENSOR, W4A8 : xq = e4m3(sat(x / a1)), x_scale unused (may be NULL);
  *   FP8_BLOCK        : per token and 128 columns s = amax/448 (1 if amax = 0),

@@ -5,7 +5,7 @@ A thin ctypes binding over the C ABI of ``libmoe.so`` (declared in
 this module only turns torch tensors into device pointers and the current
 HIP stream, and raises on a non-zero status.  There is no fallback: importing
 the package fails if the library has not been built
-(``python -m mixture_experts_layer_09_amd.build``).
+(``python mixture_experts_layer_09_amd/build.py``).
 """
 import ctypes
 import os
@@ -25,7 +25,7 @@ EXPORTS = (
     "moe_status_string", "moe_last_error", "moe_validate", "moe_padded_intermediate",
     "moe_block_m", "moe_max_blocks", "moe_max_padded_rows", "moe_align_workspace_bytes",
     "moe_combine_workspace_bytes", "moe_workspace_bytes", "moe_packed_bytes",
-    "moe_pack_w13", "moe_pack_w2", "moe_route", "moe_align", "moe_quant_act",
+    "moe_pack_w13", "moe_pack_w2", "moe_route", "moe_align", "moe_prepare", "moe_quant_act",
     "moe_gemm1_act", "moe_gemm2_combine", "moe_forward",
 )
 HOST_ONLY = EXPORTS[:11]
@@ -76,6 +76,8 @@ def _declare(lib, host_only=False):
         "moe_pack_w2": (ctypes.c_int, [_P, _VP, _I32, _VP, _VP, _VP, _VP]),
         "moe_route": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP]),
         "moe_align": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+        "moe_prepare": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                       _VP, _SZ, _VP]),
         "moe_quant_act": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP]),
         "moe_gemm1_act": (ctypes.c_int, [_P, _VP, _VP, ctypes.POINTER(Weights), _VP, _VP, _VP,
                                          _VP, _VP, _VP]),
@@ -102,7 +104,7 @@ def _hip_runtimes():
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m mixture_experts_layer_09_amd.build`")
+            f"{LIB_PATH} is missing: build it with `python mixture_experts_layer_09_amd/build.py`")
     # torch ships its own HIP runtime.  Loading it first makes libmoe.so bind to
     # that same runtime (same soname) instead of mapping a second one, so that
     # torch's device memory and streams and the library's kernels live in one
@@ -222,6 +224,16 @@ def moe_align(p, topk_ids, sorted_ids, block_expert, expert_offsets, num_padded,
     return _check(lib.moe_align(ctypes.byref(p), _ptr(topk_ids), _ptr(sorted_ids),
                                 _ptr(block_expert), _ptr(expert_offsets), _ptr(num_padded),
                                 _ptr(ws), nbytes, _stream(stream)), "moe_align")
+
+
+def moe_prepare(p, logits, topk_ids, topk_w, x, a1_scale, xq, x_scale, sorted_ids,
+                block_expert, expert_offsets, num_padded, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    return _check(lib.moe_prepare(ctypes.byref(p), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                  _ptr(x), _ptr(a1_scale), _ptr(xq), _ptr(x_scale),
+                                  _ptr(sorted_ids), _ptr(block_expert), _ptr(expert_offsets),
+                                  _ptr(num_padded), _ptr(ws), nbytes, _stream(stream)),
+                  "moe_prepare")
 
 
 def moe_quant_act(p, x, a1_scale, xq, x_scale, stream=None):

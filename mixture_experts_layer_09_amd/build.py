@@ -1,6 +1,6 @@
 """Build the HIP library (libmoe.so) and the host-only planner (libmoe_plan.so).
 
-    python -m mixture_experts_layer_09_amd.build
+    python mixture_experts_layer_09_amd/build.py
 
 libmoe.so     : every .hip source plus the planner, hipcc for gfx950 only.
 libmoe_plan.so: the planner/validator alone, built with g++ (no HIP), so that

@@ -8,14 +8,18 @@
 // page, the grouped GEMM's expert_offsets / problem sizes).
 //
 // Stable ranks come from wave ballots: within a wave, the lanes holding the
-// same expert are found with one ballot per distinct expert, and a lane's rank
-// is the number of such lanes below it.  Ranks across the 16 waves of a
-// workgroup add the earlier waves' counts; across workgroups (chunks of 1024
-// assignments) a per-chunk histogram is scanned per expert.
-//   A <= 1024 : one kernel, one workgroup (decode sizes, one launch);
+// same expert are found with one ballot per distinct expert (the expert read
+// from the leader lane with v_readlane), and a lane's rank is the number of
+// such lanes below it.  Ranks across the 16 waves of a workgroup add the
+// earlier waves' counts; across workgroups (chunks of 1024 assignments) a
+// per-chunk histogram is scanned per expert.
+//   A <= 1024 : one workgroup, one launch -- and, for decode-sized batches,
+//               together with the routing and the fp8 quantisation of x in the
+//               same kernel;
 //   A >  1024 : histogram -> scan -> scatter, three launches.
 #include "moe_device.hpp"
 #include "moe_launch.hpp"
+#include "moe_route.hpp"
 
 namespace moe {
 
@@ -25,46 +29,37 @@ constexpr int kThreads = kAlignChunk;  // 1024 threads, 16 waves
 constexpr int kWaves = kThreads / 64;
 
 // Rank of this lane among the active lanes with the same expert below it, and
-// the number of active lanes with that expert.
-__device__ __forceinline__ void match_rank(int e, bool valid, int& rank, int& cnt) {
+// the number of active lanes with that expert.  The lanes sharing this lane's
+// expert are found with one ballot per bit of the expert id: a lane matches
+// when it agrees with this lane on every bit.
+__device__ __forceinline__ void match_rank(int e, bool valid, int nbits, int& rank, int& cnt) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  uint64_t todo = __ballot(valid);
-  rank = 0;
-  cnt = 0;
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const int ev = __shfl(e, leader, 64);
-    const uint64_t same = __ballot(valid && e == ev);
-    if (valid && e == ev) {
-      rank = __popcll(same & below);
-      cnt = __popcll(same);
-    }
-    todo &= ~same;
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    same &= bit ? ones : ~ones;
   }
+  rank = valid ? __popcll(same & below) : 0;
+  cnt = valid ? __popcll(same) : 0;
 }
 
+__device__ __forceinline__ int id_bits(int E) { return 32 - __clz(E > 1 ? E - 1 : 1); }
+
 // Exclusive prefix sum over the 1024 threads of the block; returns this
-// thread's prefix and writes the block total to *total.  `tmp` holds kWaves+1
-// ints of shared memory.
+// thread's prefix and writes the block total to *total.  `tmp` holds
+// kWaves + 1 ints of shared memory.
 __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
+  const int incl = wave_inclusive_scan(v);
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = tmp[w];
-      tmp[w] = run;
-      run += c;
-    }
-    tmp[kWaves] = run;
+  if (wave == 0) {
+    const int w = lane < kWaves ? tmp[lane] : 0;
+    const int wi = wave_inclusive_scan(w);
+    if (lane < kWaves) tmp[lane] = wi - w;
+    if (lane == kWaves - 1) tmp[kWaves] = wi;
   }
   __syncthreads();
   const int res = tmp[wave] + incl - v;
@@ -111,18 +106,13 @@ __device__ void fill_tail(const int* cnt, const int* off, int E, int BM, int A,
   }
 }
 
-}  // namespace
-
-// One workgroup for A <= 1024: count, offsets, stable scatter, tails.
-// Shared memory: cnt[E], off[E+1], wcnt[kWaves][E], tmp[kWaves+1].
-__global__ __launch_bounds__(kThreads) void align_small(const int32_t* __restrict__ ids,
-                                                        int A, int E, int BM,
-                                                        int32_t* __restrict__ sorted_ids,
-                                                        int32_t* __restrict__ block_expert,
-                                                        int32_t* __restrict__ g_offsets,
-                                                        int32_t* __restrict__ g_npad) {
-  extern __shared__ int smem[];
-  int* cnt = smem;
+// Whole alignment of A <= 1024 assignments held in shared memory `sids` by
+// one workgroup.  `tab` provides cnt[E], off[E+1], wcnt[kWaves][E], tmp.
+__device__ void align_in_block(const int* sids, int A, int E, int BM, int* tab,
+                               int32_t* __restrict__ sorted_ids,
+                               int32_t* __restrict__ block_expert,
+                               int32_t* __restrict__ g_offsets, int32_t* __restrict__ g_npad) {
+  int* cnt = tab;
   int* off = cnt + E;
   int* wcnt = off + E + 1;
   int* tmp = wcnt + kWaves * E;
@@ -130,15 +120,16 @@ __global__ __launch_bounds__(kThreads) void align_small(const int32_t* __restric
   for (int i = threadIdx.x; i < kWaves * E; i += kThreads) wcnt[i] = 0;
   __syncthreads();
   const int f = threadIdx.x;
-  const int e = f < A ? ids[f] : -1;
+  const int e = f < A ? sids[f] : -1;
   const bool valid = f < A && e >= 0 && e < E;
   int rank, c;
-  match_rank(e, valid, rank, c);
+  match_rank(e, valid, id_bits(E), rank, c);
   if (valid && rank == 0) wcnt[wave * E + e] = c;
   __syncthreads();
   // per expert: total count, and the earlier waves' counts in place
   for (int x = threadIdx.x; x < E; x += kThreads) {
     int run = 0;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const int v = wcnt[w * E + x];
       wcnt[w * E + x] = run;
@@ -150,6 +141,118 @@ __global__ __launch_bounds__(kThreads) void align_small(const int32_t* __restric
   padded_offsets(cnt, off, E, BM, tmp, g_offsets, g_npad);
   if (valid) sorted_ids[off[e] + wcnt[wave * E + e] + rank] = f;
   fill_tail(cnt, off, E, BM, A, sorted_ids, block_expert);
+}
+
+size_t small_tables_bytes(int E) {
+  return (size_t(E) + (E + 1) + size_t(kWaves) * E + kWaves + 1) * 4;
+}
+
+// Dynamic shared memory above the 64 KiB default needs the kernel's opt-in.
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
+
+}  // namespace
+
+// One workgroup for A <= 1024: ids to shared memory, then the alignment.
+__global__ __launch_bounds__(kThreads) void align_small(const int32_t* __restrict__ ids,
+                                                        int A, int E, int BM,
+                                                        int32_t* __restrict__ sorted_ids,
+                                                        int32_t* __restrict__ block_expert,
+                                                        int32_t* __restrict__ g_offsets,
+                                                        int32_t* __restrict__ g_npad) {
+  extern __shared__ int smem[];
+  int* sids = smem;
+  if (threadIdx.x < A) sids[threadIdx.x] = ids[threadIdx.x];
+  __syncthreads();
+  align_in_block(sids, A, E, BM, smem + kThreads, sorted_ids, block_expert, g_offsets, g_npad);
+}
+
+// The decode-size prologue in one workgroup (T <= 128, T*K' <= 1024):
+// routing (groups of L lanes per token) or the caller's ids, the fp8
+// quantisation of x, then the alignment of the ids held in shared memory.
+struct PrologueArgs {
+  const float* logits;     // null: pre-routed, ids_in given
+  const int32_t* ids_in;
+  int T, Er, top_k, n_shared;
+  float shared_gate;
+  int renorm, E, BM, H;
+  int32_t* ids;
+  float* wts;
+  int32_t* sorted_ids;
+  int32_t* block_expert;
+  int32_t* offsets;
+  int32_t* npad;
+  const uint16_t* x;       // quantisation (QM != 0)
+  const float* a1;
+  uint8_t* xq;
+  float* xs;
+};
+
+// QM: 0 no quantisation, 1 static per-tensor a1, 2 per token and 128 columns.
+template <int L, int NPL, int QM>
+__global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
+  extern __shared__ int smem[];
+  int* sids = smem;
+  const int Kp = a.top_k + a.n_shared;
+  const int wave = threadIdx.x >> 6;
+  if (a.logits) {
+    constexpr int TPW = 64 / L;
+    for (int base = 0; base < a.T; base += kWaves * TPW) {
+      const int first = base + wave * TPW;
+      if (first < a.T) {  // uniform per wave
+        const int t = first + (threadIdx.x & 63) / L;
+        const bool valid = t < a.T;
+        const int tt = valid ? t : 0;
+        route_token<L, NPL>(a.logits + size_t(tt) * a.Er, valid, a.Er, a.top_k, a.n_shared,
+                            a.shared_gate, a.renorm, a.ids + size_t(tt) * Kp,
+                            a.wts + size_t(tt) * Kp, sids + tt * Kp);
+      }
+    }
+  } else {
+    for (int f = threadIdx.x; f < a.T * Kp; f += kThreads) sids[f] = a.ids_in[f];
+  }
+  if (QM != 0) {
+    // 8 elements per thread and pass; a DPP row of 16 lanes is one 128-column group
+    const int n8 = a.T * a.H / 8;
+    const float s1 = QM == 1 ? *a.a1 : 1.f;
+    for (int base = 0; base < n8; base += kThreads) {
+      const int i = base + threadIdx.x;
+      const bool in = i < n8;
+      const u32x4 v = in ? ld16(a.x + size_t(i) * 8) : u32x4{0, 0, 0, 0};
+      float f[8];
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = bf16_to_f32(v[k] & 0xFFFFu);
+        f[2 * k + 1] = bf16_to_f32(v[k] >> 16);
+        amax = fmaxf(amax, fmaxf(fabsf(f[2 * k]), fabsf(f[2 * k + 1])));
+      }
+      float s = s1;
+      if (QM == 2) {
+        amax = fmaxf(amax, __uint_as_float(dpp<kDppXor1, 0xF>(0u, __float_as_uint(amax))));
+        amax = fmaxf(amax, __uint_as_float(dpp<kDppXor2, 0xF>(0u, __float_as_uint(amax))));
+        amax = fmaxf(amax, __uint_as_float(dpp<kDppHalfMirror, 0xF>(0u, __float_as_uint(amax))));
+        amax = fmaxf(amax, __uint_as_float(dpp<kDppMirror, 0xF>(0u, __float_as_uint(amax))));
+        s = amax > 0.f ? amax / 448.f : 1.f;
+      }
+      if (in) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = f[k] / s;
+        u32x2 o;
+        o[0] = e4m3x4(f[0], f[1], f[2], f[3]);
+        o[1] = e4m3x4(f[4], f[5], f[6], f[7]);
+        *reinterpret_cast<u32x2*>(a.xq + size_t(i) * 8) = o;
+        if (QM == 2 && (threadIdx.x & 15) == 0) a.xs[i / 16] = s;
+      }
+    }
+  }
+  __syncthreads();
+  align_in_block(sids, a.T * Kp, a.E, a.BM, smem + kThreads, a.sorted_ids, a.block_expert,
+                 a.offsets, a.npad);
 }
 
 // Chunk histogram: hist[c][e] = assignments of chunk c with expert e.
@@ -210,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void align_scatter(const int32_t* __restr
   const int e = f < A ? ids[f] : -1;
   const bool valid = f < A && e >= 0 && e < E;
   int rank, c;
-  match_rank(e, valid, rank, c);
+  match_rank(e, valid, id_bits(E), rank, c);
   if (valid && rank == 0) wcnt[wave * E + e] = c;
   __syncthreads();
   if (valid) {
@@ -225,7 +328,9 @@ hipError_t launch_align(const moe_problem& p, const Plan& q, const int32_t* ids,
                         int32_t* num_padded, int32_t* scratch, hipStream_t stream) {
   const int A = int(q.A), E = p.E, BM = q.BM;
   if (q.chunks <= 1) {
-    const size_t sm = (size_t(E) + (E + 1) + size_t(kWaves) * E + kWaves + 1) * 4;
+    const size_t sm = size_t(kThreads) * 4 + small_tables_bytes(E);
+    hipError_t err = allow_lds(align_small, sm);
+    if (err != hipSuccess) return err;
     align_small<<<1, kThreads, sm, stream>>>(ids, A, E, BM, sorted_ids, block_expert, offsets,
                                              num_padded);
     return hipGetLastError();
@@ -234,9 +339,82 @@ hipError_t launch_align(const moe_problem& p, const Plan& q, const int32_t* ids,
   const size_t sm_scan = (size_t(E) + (E + 1) + kWaves + 1) * 4;
   align_scan<<<1, kThreads, sm_scan, stream>>>(scratch, q.chunks, A, E, BM, sorted_ids,
                                                block_expert, offsets, num_padded);
+  hipError_t err = allow_lds(align_scatter, size_t(kWaves) * E * 4);
+  if (err != hipSuccess) return err;
   align_scatter<<<q.chunks, kThreads, size_t(kWaves) * E * 4, stream>>>(ids, A, E, scratch,
                                                                           sorted_ids);
   return hipGetLastError();
+}
+
+namespace {
+template <int L, int QM>
+hipError_t prologue_l(const PrologueArgs& a, size_t sm, hipStream_t stream) {
+  const int npl = (a.Er + L - 1) / L;
+#define MOE_PRO(N)                                                                 \
+  do {                                                                             \
+    hipError_t err = allow_lds(prologue_small<L, N, QM>, sm);                      \
+    if (err != hipSuccess) return err;                                             \
+    prologue_small<L, N, QM><<<1, kThreads, sm, stream>>>(a);                      \
+  } while (0)
+  if (npl <= 1) MOE_PRO(1);
+  else if (npl <= 2) MOE_PRO(2);
+  else if (npl <= 4) MOE_PRO(4);
+  else if (npl <= 8) MOE_PRO(8);
+  else MOE_PRO(16);
+#undef MOE_PRO
+  return hipGetLastError();
+}
+
+template <int QM>
+hipError_t prologue_q(const moe_problem& p, const PrologueArgs& a, size_t sm,
+                      hipStream_t stream) {
+  return route_in_rows(p) ? prologue_l<16, QM>(a, sm, stream) : prologue_l<64, QM>(a, sm, stream);
+}
+}  // namespace
+
+bool prologue_fits(const moe_problem& p, const Plan& q) {
+  return q.chunks <= 1 && p.T <= 128 && p.E_routed <= kMaxRouted;
+}
+
+hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* logits,
+                           int32_t* ids, float* w, const uint16_t* x, const float* a1,
+                           uint8_t* xq, float* xs, bool quantise, int32_t* sorted_ids,
+                           int32_t* block_expert, int32_t* offsets, int32_t* num_padded,
+                           int32_t* scratch, hipStream_t stream) {
+  if (!prologue_fits(p, q)) {
+    hipError_t err = hipSuccess;
+    if (logits) err = launch_route(p, logits, ids, w, stream);
+    if (err != hipSuccess) return err;
+    err = launch_align(p, q, ids, sorted_ids, block_expert, offsets, num_padded, scratch, stream);
+    if (err != hipSuccess || !quantise) return err;
+    return launch_quant_act(p, x, a1, xq, xs, stream);
+  }
+  PrologueArgs a{};
+  a.logits = logits;
+  a.ids_in = ids;
+  a.T = p.T;
+  a.Er = p.E_routed;
+  a.top_k = p.top_k;
+  a.n_shared = p.n_shared;
+  a.shared_gate = p.shared_gate;
+  a.renorm = p.renormalize;
+  a.E = p.E;
+  a.BM = q.BM;
+  a.H = p.H;
+  a.ids = ids;
+  a.wts = w;
+  a.sorted_ids = sorted_ids;
+  a.block_expert = block_expert;
+  a.offsets = offsets;
+  a.npad = num_padded;
+  a.x = x;
+  a.a1 = a1;
+  a.xq = xq;
+  a.xs = xs;
+  const size_t sm = size_t(kThreads) * 4 + small_tables_bytes(p.E);
+  if (!quantise) return prologue_q<0>(p, a, sm, stream);
+  if (p.quant == MOE_QUANT_FP8_BLOCK) return prologue_q<2>(p, a, sm, stream);
+  return prologue_q<1>(p, a, sm, stream);
 }
 
 }  // namespace moe

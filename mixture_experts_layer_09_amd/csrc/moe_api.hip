@@ -124,6 +124,47 @@ int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* sorted_ids
                     "moe_align");
 }
 
+int moe_prepare(const moe_problem* p, const float* logits, int32_t* topk_ids, float* topk_w,
+                const uint16_t* x, const float* a1_scale, uint8_t* xq, float* x_scale,
+                int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                int32_t* num_padded, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe::clear_error();
+  moe::Plan q;
+  int st = moe::make_plan(p, &q);
+  if (st != MOE_OK) return st;
+  if (logits && p->E_routed > moe::kMaxRouted)
+    return moe::fail(MOE_ERR_UNSUPPORTED, "routing handles at most 1024 routed experts");
+  if (!expert_offsets) return null_arg("expert_offsets");
+  if (!num_padded) return null_arg("num_padded");
+  const bool quantise = x && p->quant != MOE_QUANT_BF16;
+  if (q.A > 0) {
+    if (!topk_ids) return null_arg("topk_ids");
+    if (logits && !topk_w) return null_arg("topk_w");
+    if (!sorted_ids) return null_arg("sorted_ids");
+    if (!block_expert) return null_arg("block_expert");
+    if (quantise) {
+      if (!xq) return null_arg("xq");
+      if (p->quant == MOE_QUANT_FP8_BLOCK && !x_scale) return null_arg("x_scale");
+      if (fp8_static(p->quant) && !a1_scale) return null_arg("a1_scale");
+    }
+  }
+  if (q.chunks > 1) {
+    if (!ws) return null_arg("ws");
+    if (ws_bytes < q.align_ws) return moe::fail(MOE_ERR_WORKSPACE, "align workspace too small");
+  }
+  clear_stale_launch_error();
+  if (q.A == 0)
+    return hip_status(moe::launch_align(*p, q, topk_ids, sorted_ids, block_expert,
+                                        expert_offsets, num_padded, static_cast<int32_t*>(ws),
+                                        (hipStream_t)stream),
+                      "moe_prepare");
+  return hip_status(moe::launch_prologue(*p, q, logits, topk_ids, topk_w, x, a1_scale, xq,
+                                         x_scale, quantise, sorted_ids, block_expert,
+                                         expert_offsets, num_padded, static_cast<int32_t*>(ws),
+                                         (hipStream_t)stream),
+                    "moe_prepare");
+}
+
 int moe_quant_act(const moe_problem* p, const uint16_t* x, const float* a1_scale, uint8_t* xq,
                   float* x_scale, moe_stream_t stream) {
   moe::clear_error();
@@ -233,17 +274,12 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const uint16_t* x,
   hipStream_t s = (hipStream_t)stream;
   clear_stale_launch_error();
 
-  if (logits && (st = hip_status(moe::launch_route(*p, logits, ids, wts, s), "route")) != MOE_OK)
+  const bool quantise = p->quant != MOE_QUANT_BF16;
+  if ((st = hip_status(moe::launch_prologue(*p, q, logits, ids, wts, x, w->a1_scale, xq, xs,
+                                            quantise, sorted, bexp, offs, npad, scratch, s),
+                       "route/align/quantise")) != MOE_OK)
     return st;
-  if ((st = hip_status(moe::launch_align(*p, q, ids, sorted, bexp, offs, npad, scratch, s),
-                       "align")) != MOE_OK)
-    return st;
-  const void* xin = x;
-  if (p->quant != MOE_QUANT_BF16) {
-    if ((st = hip_status(moe::launch_quant_act(*p, x, w->a1_scale, xq, xs, s), "quant")) != MOE_OK)
-      return st;
-    xin = xq;
-  }
+  const void* xin = quantise ? static_cast<const void*>(xq) : static_cast<const void*>(x);
   if ((st = hip_status(moe::launch_gemm1(*p, q, xin, xs, *w, sorted, bexp, npad, a2, a2s, s),
                        "gemm1")) != MOE_OK)
     return st;

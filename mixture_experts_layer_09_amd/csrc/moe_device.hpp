@@ -108,4 +108,65 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// ---------------------------------------------------------------- DPP
+// Wave64 reductions and scans through DPP lane permutes (register to
+// register, no LDS round trip): within each row of 16 lanes quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror and row_mirror bring every
+// lane the row's result; row_bcast:15 and row_bcast:31 then carry rows 0-2
+// into row 3, whose last lane (63) ends with the whole wave's result.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, ROW_MASK, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+  const uint32_t lo = uint32_t(k), hi = uint32_t(k >> 32);
+  const uint64_t o = (uint64_t(dpp<CTRL, ROW_MASK>(hi, hi)) << 32) | dpp<CTRL, ROW_MASK>(lo, lo);
+  return o > k ? o : k;
+}
+
+// Maximum of a 64-bit key over the wave, returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = dpp_max_step<kDppXor1, 0xF>(k);
+  k = dpp_max_step<kDppXor2, 0xF>(k);
+  k = dpp_max_step<kDppHalfMirror, 0xF>(k);
+  k = dpp_max_step<kDppMirror, 0xF>(k);
+  k = dpp_max_step<kDppBcast15, 0xA>(k);
+  k = dpp_max_step<kDppBcast31, 0xC>(k);
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(k), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(k >> 32), 63);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_step(float v) {
+  return v + __uint_as_float(dpp<CTRL, ROW_MASK>(0u, __float_as_uint(v)));
+}
+
+// Sum of a float over the wave, returned to every lane.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __uint_as_float(dpp<kDppXor1, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppXor2, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppHalfMirror, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppMirror, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppBcast15, 0xA>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppBcast31, 0xC>(0u, __float_as_uint(v)));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+// Inclusive prefix sum of an int over the wave (lane i gets lanes 0..i).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += int(dpp<kDppShr1, 0xF>(0u, uint32_t(v)));
+  v += int(dpp<kDppShr2, 0xF>(0u, uint32_t(v)));
+  v += int(dpp<kDppShr4, 0xF>(0u, uint32_t(v)));
+  v += int(dpp<kDppShr8, 0xF>(0u, uint32_t(v)));
+  v += int(dpp<kDppBcast15, 0xA>(0u, uint32_t(v)));
+  v += int(dpp<kDppBcast31, 0xC>(0u, uint32_t(v)));
+  return v;
+}
+
 }  // namespace moe

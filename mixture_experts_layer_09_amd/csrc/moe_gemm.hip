@@ -20,42 +20,12 @@
 // fragments (1 or 2 KiB per wave load); several k-steps of fragments are in
 // flight per wave.
 #include "moe_device.hpp"
+#include "moe_gemm_common.hpp"
 #include "moe_launch.hpp"
 
 namespace moe {
 
 namespace {
-
-struct GemmArgs {
-  const uint8_t* b;          // B rows: GEMM1 x [T][K], GEMM2 a2 [rows][K]
-  const float* b_scale;      // FP8_BLOCK: per B row per 128 K
-  const uint8_t* w;          // packed weights
-  const float* w_scale;      // packed scales
-  const float* a1;           // static x scale (FP8_TENSOR, W4A8)
-  const float* a2;           // static intermediate scale (FP8_TENSOR, W4A8)
-  const int32_t* sorted_ids;
-  const int32_t* block_expert;
-  const int32_t* num_padded;
-  const float* topk_w;       // GEMM2
-  uint8_t* out;              // GEMM1: a2 [rows][I]; GEMM2: y fp32 [A][H]
-  float* out_scale;          // GEMM1 FP8_BLOCK: [rows][I/128]
-  int K, N, I, H, Kp, A, steps, tiles;
-};
-
-template <int Q> struct QT;
-template <> struct QT<MOE_QUANT_BF16> {
-  static constexpr int AV = 1, BV = 1, FRAG = 1024, KSTEP = 32, EB = 2;
-};
-template <> struct QT<MOE_QUANT_FP8_TENSOR> {
-  static constexpr int AV = 2, BV = 2, FRAG = 2048, KSTEP = 128, EB = 1;
-};
-template <> struct QT<MOE_QUANT_FP8_BLOCK> {
-  static constexpr int AV = 2, BV = 2, FRAG = 2048, KSTEP = 128, EB = 1;
-};
-template <> struct QT<MOE_QUANT_W4A8> {
-  static constexpr int AV = 1, BV = 2, FRAG = 1024, KSTEP = 128, EB = 1;
-};
-
 template <int Q, int WT>
 struct Stage {
   u32x4 a[WT][QT<Q>::AV];
@@ -64,22 +34,6 @@ struct Stage {
   float ws[WT];    // FP8_BLOCK: weight block scale per tile
   f32x4 ws4[WT];   // W4A8: group scales of the lane's 4 rows per tile
 };
-
-template <int Q>
-__device__ __forceinline__ i32x8 fp8_pair(const u32x4& lo, const u32x4& hi) {
-  i32x8 r;
-  r[0] = int(lo[0]); r[1] = int(lo[1]); r[2] = int(lo[2]); r[3] = int(lo[3]);
-  r[4] = int(hi[0]); r[5] = int(hi[1]); r[6] = int(hi[2]); r[7] = int(hi[3]);
-  return r;
-}
-
-// Weight row block (128 rows, checkpoint order) of a packed W13 row tile.
-__device__ __forceinline__ int w13_row_block(int tile, int I, bool gated) {
-  if (!gated) return tile / 8;
-  const int pair = tile >> 1, half = tile & 1;
-  return (half * I + pair * 16) / 128;
-}
-
 }  // namespace
 
 template <int PHASE, int Q, int ACT, int WT, int KS>
@@ -148,13 +102,13 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < WT; ++j) acc[j] = mfma_bf16(S.a[j][0], S.b[0], acc[j]);
     } else {
-      const i32x8 bb = fp8_pair<Q>(S.b[0], S.b[1]);
+      const i32x8 bb = fp8_pair(S.b[0], S.b[1]);
 #pragma unroll
       for (int j = 0; j < WT; ++j) {
         if (Q == MOE_QUANT_FP8_TENSOR) {
-          acc[j] = mfma_fp8(fp8_pair<Q>(S.a[j][0], S.a[j][1]), bb, acc[j]);
+          acc[j] = mfma_fp8(fp8_pair(S.a[j][0], S.a[j][1]), bb, acc[j]);
         } else if (Q == MOE_QUANT_FP8_BLOCK) {
-          const f32x4 p = mfma_fp8(fp8_pair<Q>(S.a[j][0], S.a[j][1]), bb, f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 p = mfma_fp8(fp8_pair(S.a[j][0], S.a[j][1]), bb, f32x4{0.f, 0.f, 0.f, 0.f});
           const float sc = S.bs * S.ws[j];
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(p[i], sc, acc[j][i]);
@@ -387,6 +341,11 @@ hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, cons
   a.A = int(q.A);
   a.steps = q.ksteps_h;
   a.tiles = q.N1 / 16;
+  if (q.g1.kind == 1) {
+    a.slices = (a.tiles + 4 * q.g1.wt - 1) / (4 * q.g1.wt);
+    a.nwg = int(q.max_blocks) * a.slices;
+    return launch_gemm_tiled(1, p, q.g1, a, stream);
+  }
   const dim3 grid = stream_grid(q.g1, a.tiles, q.max_blocks);
   if (q.gated) return dispatch_quant<1, MOE_ACT_SILU_GATED>(p.quant, q.g1, grid, a, stream);
   return dispatch_quant<1, MOE_ACT_RELU2>(p.quant, q.g1, grid, a, stream);
@@ -417,6 +376,11 @@ hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, con
   a.A = int(q.A);
   a.steps = q.ksteps_i;
   a.tiles = p.H / 16;
+  if (q.g2.kind == 1) {
+    a.slices = (a.tiles + 4 * q.g2.wt - 1) / (4 * q.g2.wt);
+    a.nwg = int(q.max_blocks) * a.slices;
+    return launch_gemm_tiled(2, p, q.g2, a, stream);
+  }
   const dim3 grid = stream_grid(q.g2, a.tiles, q.max_blocks);
   return dispatch_quant<2, 0>(p.quant, q.g2, grid, a, stream);
 }

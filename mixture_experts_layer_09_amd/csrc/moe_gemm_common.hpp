@@ -1,0 +1,61 @@
+// Pieces shared by the grouped GEMM kernels.
+#pragma once
+
+#include "moe_device.hpp"
+#include "moe_plan.hpp"
+
+namespace moe {
+
+struct GemmArgs {
+  const uint8_t* b;          // B rows: GEMM1 x [T][K], GEMM2 a2 [rows][K]
+  const float* b_scale;      // FP8_BLOCK: per B row per 128 K
+  const uint8_t* w;          // packed weights
+  const float* w_scale;      // packed scales
+  const float* a1;           // static x scale (FP8_TENSOR, W4A8)
+  const float* a2;           // static intermediate scale (FP8_TENSOR, W4A8)
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  const float* topk_w;       // GEMM2
+  uint8_t* out;              // GEMM1: a2 [rows][I]; GEMM2: y fp32 [A][H]
+  float* out_scale;          // GEMM1 FP8_BLOCK: [rows][I/128]
+  int K, N, I, H, Kp, A, steps, tiles;
+  int slices;                // tiled kernel: workgroups along the weight rows
+  int nwg;                   // tiled kernel: real workgroups (grid is padded to 8)
+};
+
+// Per-format constants: u32x4 loads per A / B fragment, bytes per A
+// fragment, K elements per MFMA k-step, B element bytes.
+template <int Q> struct QT;
+template <> struct QT<MOE_QUANT_BF16> {
+  static constexpr int AV = 1, BV = 1, FRAG = 1024, KSTEP = 32, EB = 2;
+};
+template <> struct QT<MOE_QUANT_FP8_TENSOR> {
+  static constexpr int AV = 2, BV = 2, FRAG = 2048, KSTEP = 128, EB = 1;
+};
+template <> struct QT<MOE_QUANT_FP8_BLOCK> {
+  static constexpr int AV = 2, BV = 2, FRAG = 2048, KSTEP = 128, EB = 1;
+};
+template <> struct QT<MOE_QUANT_W4A8> {
+  static constexpr int AV = 1, BV = 2, FRAG = 1024, KSTEP = 128, EB = 1;
+};
+
+__device__ __forceinline__ i32x8 fp8_pair(const u32x4& lo, const u32x4& hi) {
+  i32x8 r;
+  r[0] = int(lo[0]); r[1] = int(lo[1]); r[2] = int(lo[2]); r[3] = int(lo[3]);
+  r[4] = int(hi[0]); r[5] = int(hi[1]); r[6] = int(hi[2]); r[7] = int(hi[3]);
+  return r;
+}
+
+// Weight row block (128 rows, checkpoint order) of a packed W13 row tile.
+__device__ __forceinline__ int w13_row_block(int tile, int I, bool gated) {
+  if (!gated) return tile / 8;
+  const int pair = tile >> 1, half = tile & 1;
+  return (half * I + pair * 16) / 128;
+}
+
+// The tiled (prefill) kernels; `a.slices` and `a.nwg` must be set.
+hipError_t launch_gemm_tiled(int phase, const moe_problem& p, const GemmCfg& c,
+                             const GemmArgs& a, hipStream_t st);
+
+}  // namespace moe

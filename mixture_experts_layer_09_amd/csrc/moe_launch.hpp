@@ -16,6 +16,21 @@ hipError_t launch_align(const moe_problem& p, const Plan& q, const int32_t* ids,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
                         int32_t* num_padded, int32_t* scratch, hipStream_t stream);
 
+// Whether the routing runs one token per 16-lane row (else per wave).
+bool route_in_rows(const moe_problem& p);
+
+// Whether the decode-size prologue (one workgroup) takes the whole batch.
+bool prologue_fits(const moe_problem& p, const Plan& q);
+
+// Routing (when logits is not null; else ids are the caller's), alignment,
+// and with `quantise` the fp8 quantisation of x -- one kernel for
+// decode-sized batches, the separate kernels otherwise.
+hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* logits,
+                           int32_t* ids, float* w, const uint16_t* x, const float* a1,
+                           uint8_t* xq, float* xs, bool quantise, int32_t* sorted_ids,
+                           int32_t* block_expert, int32_t* offsets, int32_t* num_padded,
+                           int32_t* scratch, hipStream_t stream);
+
 hipError_t launch_quant_act(const moe_problem& p, const uint16_t* x, const float* a1,
                             uint8_t* xq, float* xs, hipStream_t stream);
 

@@ -109,8 +109,9 @@ int make_plan(const moe_problem* p, Plan* plan) {
                   p->I, ip);
     return fail(MOE_ERR_ALIGNMENT, buf);
   }
-  if (p->block_m != 0 && p->block_m != 16 && p->block_m != 64 && p->block_m != 128)
-    return fail(MOE_ERR_INVALID_ARG, "block_m must be 0, 16, 64 or 128");
+  if (p->block_m != 0 && p->block_m != 16 && p->block_m != 64 && p->block_m != 128 &&
+      p->block_m != 256)
+    return fail(MOE_ERR_INVALID_ARG, "block_m must be 0, 16, 64, 128 or 256");
 
   Plan q;
   q.Kp = p->top_k + p->n_shared;
@@ -124,14 +125,19 @@ int make_plan(const moe_problem* p, Plan* plan) {
     return fail(MOE_ERR_UNSUPPORTED, "weights too large");
 
   // ---- tile table: the alignment block follows the expected rows per
-  // expert; decode-sized problems stream weights 16 token-rows at a time.
+  // expert.  Decode-sized problems stream weights 16 token rows at a time;
+  // with many rows per expert the tiled kernels stage 128 token rows in LDS
+  // and reuse every weight fragment across them.
+  const int64_t rows_per_expert = q.A / std::max(1, p->E);
   if (p->block_m != 0) {
     q.BM = p->block_m;
+  } else if (rows_per_expert >= kTiledMinRows) {
+    q.BM = 128;
   } else {
     q.BM = 16;
   }
-  if (q.BM != 16)
-    return fail(MOE_ERR_UNSUPPORTED, "only block_m = 16 is built in this version");
+  if (q.BM == 256 && p->quant != MOE_QUANT_FP8_TENSOR)
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = 256 runs for the fp8 per-tensor mode only");
   const int64_t nz = std::min<int64_t>(p->E, q.A);
   q.max_blocks = std::min<int64_t>(q.A, (q.A + nz * (q.BM - 1)) / q.BM);
   q.max_rows = q.max_blocks * q.BM;
@@ -146,8 +152,13 @@ int make_plan(const moe_problem* p, Plan* plan) {
   q.ksteps_i = p->I / q.kstep;
   q.a2_elem = p->quant == MOE_QUANT_BF16 ? 2 : 1;
   const int64_t blocks_est = std::max<int64_t>(1, std::min<int64_t>(q.max_blocks, nz));
-  q.g1 = pick_stream(blocks_est, q.N1, p->quant == MOE_QUANT_FP8_BLOCK);
-  q.g2 = pick_stream(blocks_est, p->H, false);
+  if (q.BM == 16) {
+    q.g1 = pick_stream(blocks_est, q.N1, p->quant == MOE_QUANT_FP8_BLOCK);
+    q.g2 = pick_stream(blocks_est, p->H, false);
+  } else {
+    q.g1 = GemmCfg{1, q.BM / 16, 4, 1, 4};
+    q.g2 = q.g1;
+  }
 
   // ---- scratch sizes and the moe_forward workspace layout
   q.align_ws = q.chunks > 1 ? align256(size_t(q.chunks) * p->E * 4) : 256;

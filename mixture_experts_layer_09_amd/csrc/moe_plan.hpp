@@ -15,6 +15,7 @@ constexpr int kGroup = 128;        // block / group width of the quantised forma
 constexpr int kAlignChunk = 1024;  // assignments per workgroup in the align kernels
 constexpr int kMaxRouted = 1024;   // logits per token the routing kernel holds
 constexpr int kMaxSlots = 64;      // K' = top_k + n_shared limit (one lane each)
+constexpr int kTiledMinRows = 48;  // rows per expert from which the tiled GEMMs run
 
 // Which GEMM kernel runs and how it is tiled.
 //  kind 0: weight-streaming kernel, one 16-row block of tokens per workgroup,

@@ -1,0 +1,112 @@
+// One token's routing by a group of L lanes (L = 16: a DPP row, four tokens
+// per wave; L = 64: the whole wave).  Shared by the routing kernel and the
+// fused decode prologue kernel.
+#pragma once
+
+#include "moe_device.hpp"
+
+namespace moe {
+
+// Unsigned integer with the same order as the float (+0.0 and -0.0 equal).
+__device__ __forceinline__ uint32_t float_order_bits(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);  // -0.0 + 0.0 = +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float float_from_order_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Maximum of a 64-bit key over the lane group; every lane of the group gets it.
+template <int L>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t k) {
+  k = dpp_max_step<kDppXor1, 0xF>(k);
+  k = dpp_max_step<kDppXor2, 0xF>(k);
+  k = dpp_max_step<kDppHalfMirror, 0xF>(k);
+  k = dpp_max_step<kDppMirror, 0xF>(k);
+  if (L == 16) return k;
+  k = dpp_max_step<kDppBcast15, 0xA>(k);
+  k = dpp_max_step<kDppBcast31, 0xC>(k);
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(k), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(k >> 32), 63);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Sum over the lane group; every lane of the group gets it.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if (L == 64) return wave_sum_dpp(v);
+  v += __uint_as_float(dpp<kDppXor1, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppXor2, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppHalfMirror, 0xF>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kDppMirror, 0xF>(0u, __float_as_uint(v)));
+  return v;
+}
+
+// Routes the token whose Er logits start at `row` (Er <= L * NPL, K' <= L):
+// writes K' = top_k + n_shared ids and weights to ids_out / w_out (and the
+// ids to lds_ids when it is not null).  Called by all lanes of the group, with
+// every lane of the wave active.  `valid` false makes the group compute
+// without reading or writing (for the groups past the last token).
+template <int L, int NPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, bool valid, int Er,
+                                            int top_k, int n_shared, float shared_gate,
+                                            int renorm, int32_t* __restrict__ ids_out,
+                                            float* __restrict__ w_out, int* lds_ids) {
+  const int gl = threadIdx.x & (L - 1);  // lane within the group
+  uint64_t key[NPL];
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int j = gl + L * i;
+    const bool in = valid && j < Er;
+    v[i] = in ? row[j] : 0.f;
+    key[i] = in ? (uint64_t(float_order_bits(v[i])) << 32) | uint32_t(~uint32_t(j)) : 0;
+  }
+  float my_val = 0.f;  // lane r of the group keeps the r-th selected logit
+  int my_idx = 0;
+  float vmax = 0.f;
+  for (int r = 0; r < top_k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) best = key[i] > best ? key[i] : best;
+    const uint64_t w = group_max_u64<L>(best);
+    const int j = int(~uint32_t(w));
+    const float val = float_from_order_bits(uint32_t(w >> 32));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (j == gl + L * i) key[i] = 0;
+    if (r == 0) vmax = val;  // the first pick is the largest logit
+    if (gl == r) {
+      my_val = val;
+      my_idx = j;
+    }
+  }
+  float denom;
+  if (renorm) {
+    denom = group_sum<L>(gl < top_k ? expf(my_val - vmax) : 0.f);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (valid && gl + L * i < Er) s += expf(v[i] - vmax);
+    denom = group_sum<L>(s);
+  }
+  const int Kp = top_k + n_shared;
+  if (valid && gl < Kp) {
+    int id;
+    float wt;
+    if (gl < top_k) {
+      id = my_idx;
+      wt = expf(my_val - vmax) / denom;
+    } else {
+      id = Er + (gl - top_k);
+      wt = shared_gate;
+    }
+    ids_out[gl] = id;
+    w_out[gl] = wt;
+    if (lds_ids) lds_ids[gl] = id;
+  }
+}
+
+}  // namespace moe

@@ -6,7 +6,7 @@ import torch
 
 from . import (combine_workspace_bytes, max_blocks, max_padded_rows, moe_align,
                moe_forward, moe_gemm1_act, moe_gemm2_combine, moe_pack_w2, moe_pack_w13,
-               moe_quant_act, moe_route, packed_bytes, problem, align_workspace_bytes,
+               moe_quant_act, moe_route, moe_prepare, packed_bytes, problem, align_workspace_bytes,
                workspace_bytes, weights)
 
 
@@ -92,6 +92,13 @@ class MoELayer:
 
     def route(self, T, logits, b):
         moe_route(self.problem(T), logits, b["topk_ids"], b["topk_w"])
+
+    def prepare(self, T, logits, x, b):
+        """Routing, fp8 quantisation of x and alignment (one launch at decode sizes)."""
+        moe_prepare(self.problem(T), logits, b["topk_ids"], b["topk_w"],
+                    None if self.kw["quant"] == "bf16" else x, self.a1, b["xq"], b["xs"],
+                    b["sorted_ids"], b["block_expert"], b["offsets"], b["num_padded"],
+                    b["align_ws"])
 
     def align(self, T, b):
         moe_align(self.problem(T), b["topk_ids"], b["sorted_ids"], b["block_expert"],

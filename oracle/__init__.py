@@ -37,5 +37,6 @@ from .moe import (  # noqa: F401
     dequant_w13,
     dequant_w2,
     store_intermediate,
+    flip_margin,
     moe_forward,
 )

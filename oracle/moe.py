@@ -280,6 +280,43 @@ def store_intermediate(a, quant, a2=None):
     raise ValueError(quant)
 
 
+# Rounding decisions of the fp8 intermediate that fp32 accumulation in another
+# order can take either way: values within this relative distance (plus the
+# same absolute amount, for values near zero) of a rounding boundary.
+FLIP_REL = 2.0 ** -12
+
+
+def flip_margin(a, quant, a2=None):
+    """Per intermediate value: the change one e4m3 rounding flip can make.
+
+    For the fp8 storage modes, the exact quotient q = a / s (s = a2, or the
+    row's per-128-column scale) is compared with the midpoints between
+    adjacent e4m3 values (the rounding boundaries; the saturated range above
+    448 has none).  Where q lies within FLIP_REL * (|q| + 1) of a boundary,
+    either neighbouring code is a correct rounding of a value the kernels may
+    have accumulated in fp32; the margin is the gap between the two codes,
+    in the intermediate's units.  Elsewhere, and for bf16 / exact storage,
+    the margin is 0.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    if quant in ("fp8_tensor", "w4a8"):
+        s = np.full(a.shape, float(np.float32(a2)))
+    elif quant == "fp8_block":
+        _, sg = quant_fp8_group(a)
+        s = np.repeat(sg.astype(np.float64), GROUP, axis=1)
+    else:
+        return np.zeros_like(a)
+    q = np.abs(a / s)
+    pos = e4m3_decode(np.arange(127, dtype=np.uint8))        # 0 .. 448, increasing
+    mids = (pos[1:] + pos[:-1]) / 2.0                        # boundary i: pos[i] | pos[i+1]
+    gaps = pos[1:] - pos[:-1]
+    i = np.clip(np.searchsorted(mids, q), 1, mids.size - 1)
+    near = np.where(np.abs(q - mids[i - 1]) <= np.abs(q - mids[i]), i - 1, i)
+    d = np.abs(q - mids[near])
+    amb = d <= FLIP_REL * (q + 1.0)
+    return np.where(amb, gaps[near] * s, 0.0)
+
+
 def _silu(g):
     return g / (1.0 + np.exp(-g))
 
@@ -304,7 +341,7 @@ def _activate(h, act, I, layout_g):
 def moe_forward(x, w13, w2, *, quant, act, E_routed, top_k, renormalize,
                 n_shared=0, shared_gate=1.0, logits=None, topk_ids=None,
                 topk_w=None, w13_scale=None, w2_scale=None, a1=None, a2=None,
-                layout_g=None, storage=None):
+                layout_g=None, storage=None, with_margin=False):
     """Route, then per expert: dequantise-then-matmul in fp64.
 
     x: [T, H] float (bf16 values).  w13/w2: stored codes in the split layout
@@ -312,7 +349,10 @@ def moe_forward(x, w13, w2, *, quant, act, E_routed, top_k, renormalize,
     (``topk_ids``, ``topk_w``) is given.  ``storage`` overrides how the
     intermediate is rounded ("exact" keeps fp64; default: the quant mode).
 
-    Returns dict(out fp64 [T, H], topk_ids, topk_w, xq, xs).
+    Returns dict(out fp64 [T, H], topk_ids, topk_w, xq, xs) and, with
+    ``with_margin``, ``margin`` [T, H]: for each output the largest change
+    that rounding flips of ambiguous intermediate values (``flip_margin``)
+    can make, sum over them of routing weight * gap * |W2 entry|.
     """
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
@@ -328,6 +368,7 @@ def moe_forward(x, w13, w2, *, quant, act, E_routed, top_k, renormalize,
     xd = dequant_x(x, quant, xq, xs, a1)
     st = storage if storage is not None else quant
     out = np.zeros((T, H), dtype=np.float64)
+    margin = np.zeros((T, H), dtype=np.float64) if with_margin else None
     flat_ids = ids.reshape(-1)
     flat_w = wts.reshape(-1)
     for e in range(E):
@@ -340,8 +381,13 @@ def moe_forward(x, w13, w2, *, quant, act, E_routed, top_k, renormalize,
         I = W2.shape[1]
         h = xd[t] @ W13.T
         a = _activate(h, act, I, layout_g if gated else None)
+        if with_margin:
+            mg = flip_margin(a, st, a2) @ np.abs(W2).T
+            np.add.at(margin, t, np.abs(flat_w[f])[:, None] * mg)
         a = store_intermediate(a, st, a2)
         y = a @ W2.T
         np.add.at(out, t, flat_w[f][:, None] * y)
-    return {"out": out, "topk_ids": ids.astype(np.int32), "topk_w": wts,
-            "xq": xq, "xs": xs}
+    res = {"out": out, "topk_ids": ids.astype(np.int32), "topk_w": wts, "xq": xq, "xs": xs}
+    if with_margin:
+        res["margin"] = margin
+    return res

@@ -67,25 +67,36 @@ def oracle_forward(cfg: MoEConfig, W, x_bits, logits=None, a1=None, a2=None, top
         x, W["w13"], W["w2"], quant=cfg.quant, act=cfg.act, E_routed=cfg.E_routed,
         top_k=cfg.top_k, renormalize=cfg.renormalize, n_shared=cfg.n_shared,
         shared_gate=cfg.shared_gate, logits=logits, topk_ids=topk_ids, topk_w=topk_w,
-        w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], a1=a1, a2=a2, **kw)
+        w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], a1=a1, a2=a2, with_margin=True, **kw)
 
 
-def errors(got, ref):
+def errors(got, ref, margin=None):
     got = np.asarray(got, dtype=np.float64)
-    err = got - ref
-    max_abs = float(np.abs(err).max()) if err.size else 0.0
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    beyond = err if margin is None else np.maximum(err - margin, 0.0)
+    max_beyond = float(beyond.max()) if err.size else 0.0
     nref = float(np.linalg.norm(ref))
-    rel = float(np.linalg.norm(err) / nref) if nref > 0 else float(np.linalg.norm(err))
-    return max_abs, rel
+    rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(err))
+    return max_abs, max_beyond, rel
 
 
-def assert_close(got, ref, quant, label=""):
-    max_abs, rel = errors(got, ref)
+def assert_close(got, ref, quant, label="", margin=None):
+    """max-abs 2e-2 (bf16, fp8) beyond each output's rounding-flip margin,
+    and rel-L2 1e-2 (3e-2 for int4 weights).  The margin (oracle.flip_margin)
+    is non-zero only where an fp8 intermediate value lies so close to a
+    rounding boundary that fp32 accumulation may round it the other way."""
+    if isinstance(ref, dict):
+        margin = ref.get("margin") if margin is None else margin
+        ref = ref["out"]
+    max_abs, beyond, rel = errors(got, ref, margin)
     ma, rl = TOL[quant]
-    say(f"  {label}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    nmarg = 0 if margin is None else int((margin > 0).sum())
+    say(f"  {label}: max_abs={max_abs:.3e} beyond_margin={beyond:.3e} rel_l2={rel:.3e} "
+        f"outputs_with_margin={nmarg}")
     assert np.all(np.isfinite(got)), label
     if ma is not None:
-        assert max_abs <= ma, f"{label}: max_abs {max_abs} > {ma}"
+        assert beyond <= ma, f"{label}: |err| exceeds {ma} + margin by {beyond - ma}"
     assert rel <= rl, f"{label}: rel_l2 {rel} > {rl}"
 
 

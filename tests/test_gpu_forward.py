@@ -5,7 +5,9 @@ and tiny passes are compared on every output; the full-size prefill passes
 (cfg3 M=4096, cfg4 M=128/8192, cfg5 M=8192, cfg3 M=256) run the whole pass on
 the GPU and compare a seeded sample of token rows (first and last included)
 with the oracle on those tokens.  Tolerances: max-abs 2e-2 and rel-L2 1e-2
-(bf16, fp8), rel-L2 3e-2 (int4 weights).
+(bf16, fp8), rel-L2 3e-2 (int4 weights); the max-abs bound of an output is
+widened by the oracle's flip margin where an fp8 intermediate value sits at a
+rounding boundary (either code is a correct rounding).
 """
 import numpy as np
 import pytest
@@ -46,7 +48,7 @@ def test_forward_config(cid, M, n):
     got = out.float().cpu().numpy().astype(np.float64)
     rows = _sample(M, n, 1000 * cid + M)
     ref = oracle_forward(cfg, W, tok["x_bits"][rows], tok["logits"][rows], sc["a1"], sc["a2"])
-    assert_close(got[rows], ref["out"], cfg.quant, f"{cfg.name} M={M}")
+    assert_close(got[rows], ref, cfg.quant, f"{cfg.name} M={M}")
     del layer
     torch.cuda.empty_cache()
 
@@ -71,7 +73,7 @@ def test_forward_small_ragged(quant, act, T):
     out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
     torch.cuda.synchronize()
     ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"], sc["a1"], sc["a2"])
-    assert_close(out.float().cpu().numpy(), ref["out"], quant, f"small {quant} {act} T={T}")
+    assert_close(out.float().cpu().numpy(), ref, quant, f"small {quant} {act} T={T}")
 
 
 def test_components_equal_forward():
@@ -90,6 +92,12 @@ def test_components_equal_forward():
     layer.gemm2(8, b)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), b["out"].view(torch.int16))
+    b2 = layer.buffers(8)
+    layer.prepare(8, lg, x, b2)
+    layer.gemm1(8, x, b2)
+    layer.gemm2(8, b2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), b2["out"].view(torch.int16))
 
 
 @pytest.mark.parametrize("quant", ["bf16", "fp8_block"])
@@ -110,7 +118,7 @@ def test_prerouted_with_masked_slots(quant):
     ref = oracle_forward(cfg, W, tok["x_bits"], topk_ids=ids, topk_w=w.astype(np.float64))
     got = out.float().cpu().numpy()
     assert np.all(got[3] == 0.0)
-    assert_close(got, ref["out"], quant, "prerouted")
+    assert_close(got, ref, quant, "prerouted")
 
 
 def test_pack_swap_and_padding():
@@ -129,7 +137,7 @@ def test_pack_swap_and_padding():
     out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
     torch.cuda.synchronize()
     ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"])
-    assert_close(out.float().cpu().numpy(), ref["out"], "bf16", "swap+pad")
+    assert_close(out.float().cpu().numpy(), ref, "bf16", "swap+pad")
 
 
 def test_zero_tokens_is_a_noop():
@@ -169,3 +177,26 @@ def test_invalid_call_enqueues_nothing():
     assert ei.value.status == moe.MOE_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.count_nonzero(out.float()) == 0
+
+
+TILED = [(q, a, bm) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
+         for a in ("silu", "relu2") for bm in (64, 128)]
+
+
+@pytest.mark.parametrize("quant,act,bm", TILED)
+def test_forward_tiled_ragged(quant, act, bm):
+    """The tiled (prefill) kernels on small shapes: several blocks per expert
+    with a ragged last block, three K stages, and a partly filled last weight
+    slice for the non-gated case."""
+    cfg = ad_hoc(93, quant, act, H=384, I=384, E_routed=4, top_k=2, n_shared=1)
+    say(f"tiled {quant} {act} bm={bm}")
+    W = synth.make_weights(cfg, seed=777)
+    T = 150
+    tok = synth.make_tokens(cfg, T, seed=78)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"], block_m=bm)
+    assert moe.block_m(layer.problem(T)) == bm
+    out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
+    torch.cuda.synchronize()
+    ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"], sc["a1"], sc["a2"])
+    assert_close(out.float().cpu().numpy(), ref, quant, f"tiled {quant} {act} bm={bm}")

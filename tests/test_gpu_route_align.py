@@ -127,3 +127,81 @@ def test_quant_act_bitexact(quant, T, H):
     assert np.array_equal(xq.cpu().numpy(), rq)
     if quant == "fp8_block":
         assert np.array_equal(xs.cpu().numpy(), rs)
+
+
+RA_CASES = [  # T, E_routed, top_k, n_shared, renormalize, block_m
+    (1, 128, 8, 0, True, 0), (64, 128, 8, 0, True, 0), (16, 512, 10, 1, True, 0),
+    (64, 8, 2, 0, False, 0), (128, 128, 6, 0, True, 0), (93, 1000, 11, 0, True, 0),
+    (256, 512, 10, 1, True, 0), (4096, 512, 10, 1, True, 0), (8192, 20, 8, 0, True, 0)]
+
+
+@pytest.mark.parametrize("T,Er,k,ns,renorm,bm", RA_CASES)
+def test_prepare_route_align_bitexact(T, Er, k, ns, renorm, bm):
+    """moe_prepare (one launch at decode sizes) equals the oracle's routing
+    followed by its alignment."""
+    say(f"route_align T={T} Er={Er} k={k} ns={ns}")
+    rng = np.random.default_rng(3 * T + Er)
+    lg = rng.standard_normal((T, Er)).astype(np.float32)
+    lg[:, ::5] = np.round(lg[:, ::5])          # some exact ties
+    p = moe.problem(T=T, H=128, I=128, E_routed=Er, top_k=k, n_shared=ns,
+                    renormalize=renorm, block_m=bm)
+    E = Er + ns
+    rows, blocks = moe.max_padded_rows(p), moe.max_blocks(p)
+    ids = torch.empty((T, k + ns), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k + ns), dtype=torch.float32, device="cuda")
+    sorted_ids = torch.full((max(rows, 1),), -7, dtype=torch.int32, device="cuda")
+    bexp = torch.full((max(blocks, 1),), -7, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    npad = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(moe.align_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+    moe.moe_prepare(p, dev(lg), ids, w, None, None, None, None, sorted_ids, bexp, offs, npad, ws)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(lg, k, renorm, ns, 1.0)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-5, atol=1e-7)
+    bmr = moe.block_m(p)
+    ref = oracle.align(rid, E, bmr)
+    n = int(npad.item())
+    assert n == ref["num_padded"]
+    assert np.array_equal(offs.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(sorted_ids.cpu().numpy()[:n], ref["sorted_ids"])
+    assert np.array_equal(bexp.cpu().numpy()[:n // bmr], ref["block_expert"])
+
+
+@pytest.mark.parametrize("quant,T,H,Er,k,ns", [("fp8_block", 16, 2048, 512, 10, 1),
+                                               ("fp8_tensor", 1, 4096, 128, 6, 0),
+                                               ("fp8_tensor", 128, 4096, 128, 6, 0),
+                                               ("w4a8", 64, 6144, 20, 8, 0),
+                                               ("fp8_block", 300, 2048, 512, 10, 1)])
+def test_prepare_quantise_equals_separate_calls(quant, T, H, Er, k, ns):
+    """moe_prepare's fused routing + quantisation + alignment is bit-identical
+    to moe_route, moe_quant_act and moe_align called one after another."""
+    say(f"prepare {quant} T={T}")
+    rng = np.random.default_rng(T + H)
+    lg = dev(rng.standard_normal((T, Er)).astype(np.float32))
+    x = dev(_bf16_bits(rng.standard_normal((T, H)) * 3))
+    a1 = torch.tensor(0.01, device="cuda")
+    p = moe.problem(T=T, H=H, I=128, E_routed=Er, top_k=k, n_shared=ns, quant=quant)
+    E, K = Er + ns, k + ns
+    rows, blocks = moe.max_padded_rows(p), moe.max_blocks(p)
+
+    def bufs():
+        return dict(ids=torch.empty((T, K), dtype=torch.int32, device="cuda"),
+                    w=torch.empty((T, K), dtype=torch.float32, device="cuda"),
+                    xq=torch.empty((T, H), dtype=torch.uint8, device="cuda"),
+                    xs=torch.zeros((T, H // 128), dtype=torch.float32, device="cuda"),
+                    si=torch.full((rows,), -7, dtype=torch.int32, device="cuda"),
+                    be=torch.full((blocks,), -7, dtype=torch.int32, device="cuda"),
+                    off=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                    np=torch.empty(1, dtype=torch.int32, device="cuda"),
+                    ws=torch.empty(max(moe.align_workspace_bytes(p), 1), dtype=torch.uint8,
+                                   device="cuda"))
+    a, b = bufs(), bufs()
+    moe.moe_prepare(p, lg, a["ids"], a["w"], x, a1, a["xq"], a["xs"], a["si"], a["be"],
+                    a["off"], a["np"], a["ws"])
+    moe.moe_route(p, lg, b["ids"], b["w"])
+    moe.moe_quant_act(p, x, a1, b["xq"], b["xs"])
+    moe.moe_align(p, b["ids"], b["si"], b["be"], b["off"], b["np"], b["ws"])
+    torch.cuda.synchronize()
+    for key in ("ids", "w", "xq", "xs", "si", "be", "off", "np"):
+        assert torch.equal(a[key], b[key]), key

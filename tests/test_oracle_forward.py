@@ -284,3 +284,52 @@ def test_fp8_block_single_expert_with_torch_casts():
     W2 = c2.double() * torch.from_numpy(k(s2))
     ref = _torch_mlp(xq.numpy(), W13.numpy(), W2.numpy(), "silu", mid=gq)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- flip margin
+def test_flip_margin_marks_boundaries_only():
+    a2 = 0.5
+    pos = codecs.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (pos[1:] + pos[:-1]) / 2
+    # exactly on a boundary: either neighbour is admissible, margin = the gap
+    on = mids[[10, 50, 100, 125]] * a2
+    got = oracle.flip_margin(on, "fp8_tensor", a2)
+    np.testing.assert_allclose(got, (pos[[11, 51, 101, 126]] - pos[[10, 50, 100, 125]]) * a2)
+    # the representable values themselves and values past 448 are unambiguous
+    assert np.all(oracle.flip_margin(pos[1:] * a2, "fp8_tensor", a2) == 0)
+    assert np.all(oracle.flip_margin(np.array([500.0, 1e4, -900.0]) * a2, "fp8_tensor", a2) == 0)
+    # no margin without fp8 storage
+    assert np.all(oracle.flip_margin(on, "bf16") == 0)
+
+
+def test_flip_margin_covers_every_flip_of_perturbed_accumulation():
+    """Perturb the intermediate by a relative 2^-16 (far more than fp32
+    accumulation error): every value whose e4m3 code changes is marked, and
+    the change of its dequantised value is within the margin."""
+    rng = R(21)
+    a = rng.standard_normal((40, 256)) * 3
+    for quant, a2 in (("fp8_tensor", 0.02), ("fp8_block", None)):
+        m = oracle.flip_margin(a, quant, a2)
+
+        def codes(v):
+            if quant == "fp8_tensor":
+                return oracle.moe.quant_fp8_tensor(v, a2), np.full(v.shape, float(np.float32(a2)))
+            c, sc = oracle.moe.quant_fp8_group(v)
+            return c, np.repeat(sc.astype(np.float64), 128, axis=1)
+        base, s0 = codes(a)
+        for sign in (1, -1):
+            pert, s1 = codes(a * (1 + sign * 2.0 ** -16))
+            changed = pert != base
+            assert np.all(m[changed] > 0)
+            gap = np.abs(codecs.e4m3_decode(pert) - codecs.e4m3_decode(base)) * s0
+            assert np.all(gap[changed] <= m[changed] * (1 + 1e-6))
+        assert (m > 0).mean() < 0.01     # ambiguity is rare
+
+
+def test_forward_margin_is_zero_for_bf16_and_bounds_flips():
+    E, H, I, T = 3, 32, 16, 8
+    w13, w2, x = _mk_bf16(E, 2 * I, H, I, T, 22)
+    lg = R(23).standard_normal((T, E)).astype(np.float32)
+    r = oracle.moe_forward(x, w13, w2, quant="bf16", act="silu", E_routed=E, top_k=2,
+                           renormalize=True, logits=lg, with_margin=True)
+    assert np.all(r["margin"] == 0)
