@@ -341,7 +341,7 @@ hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, cons
   a.A = int(q.A);
   a.steps = q.ksteps_h;
   a.tiles = q.N1 / 16;
-  if (q.g1.kind == 1) {
+  if (q.g1.kind >= 1) {
     a.slices = (a.tiles + 4 * q.g1.wt - 1) / (4 * q.g1.wt);
     a.nwg = int(q.max_blocks) * a.slices;
     return launch_gemm_tiled(1, p, q.g1, a, stream);
@@ -376,7 +376,7 @@ hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, con
   a.A = int(q.A);
   a.steps = q.ksteps_i;
   a.tiles = p.H / 16;
-  if (q.g2.kind == 1) {
+  if (q.g2.kind >= 1) {
     a.slices = (a.tiles + 4 * q.g2.wt - 1) / (4 * q.g2.wt);
     a.nwg = int(q.max_blocks) * a.slices;
     return launch_gemm_tiled(2, p, q.g2, a, stream);

@@ -156,7 +156,10 @@ int make_plan(const moe_problem* p, Plan* plan) {
     q.g1 = pick_stream(blocks_est, q.N1, p->quant == MOE_QUANT_FP8_BLOCK);
     q.g2 = pick_stream(blocks_est, p->H, false);
   } else {
-    q.g1 = GemmCfg{1, q.BM / 16, 4, 1, 4};
+    // fp8 / int4 weights at 128-row blocks: weights and tokens staged in LDS by
+    // direct-to-LDS loads, several k-steps in flight
+    const bool lds = q.BM == 128 && p->quant != MOE_QUANT_BF16;
+    q.g1 = GemmCfg{lds ? 2 : 1, q.BM / 16, 4, 1, 4};
     q.g2 = q.g1;
   }
 
