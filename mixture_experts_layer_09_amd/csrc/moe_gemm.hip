@@ -292,6 +292,8 @@ hipError_t dispatch_stream(const GemmCfg& c, dim3 grid, const GemmArgs& a, hipSt
     else if (c.wt == 4 && c.ksplit == 2) gemm_stream<PHASE, Q, ACT, 4, 2><<<grid, block, 0, st>>>(a);
     else if (c.wt == 4 && c.ksplit == 4) gemm_stream<PHASE, Q, ACT, 4, 4><<<grid, block, 0, st>>>(a);
     else if (c.wt == 2 && c.ksplit == 4) gemm_stream<PHASE, Q, ACT, 2, 4><<<grid, block, 0, st>>>(a);
+    else if (c.wt == 2 && c.ksplit == 2) gemm_stream<PHASE, Q, ACT, 2, 2><<<grid, block, 0, st>>>(a);
+    else if (c.wt == 2 && c.ksplit == 1) gemm_stream<PHASE, Q, ACT, 2, 1><<<grid, block, 0, st>>>(a);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -151,6 +151,19 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
   }
 }
 
+// Workgroup -> tile.  Workgroups are dealt to the 8 XCDs round robin; the
+// tiles of the real blocks (known on the device only) are cut into 8
+// contiguous ranges, one per XCD, so that workgroups sharing a block's token
+// rows or an expert's weights run on one L2.  Workgroups past the real tiles
+// return at once, spread over all XCDs rather than piled on the last one.
+__device__ __forceinline__ bool xcd_tile(const GemmArgs& g, int BM, int& L) {
+  const int nact = min(g.nwg, (*g.num_padded / BM) * g.slices);
+  const int per = (nact + 7) / 8;
+  const int j = blockIdx.x / 8;
+  L = (blockIdx.x % 8) * per + j;
+  return j < per && L < nact;
+}
+
 template <int PHASE, int Q, int ACT, int WT, int NT>
 __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
   using T = QT<Q>;
@@ -169,12 +182,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
   __shared__ float lds_bs[2][Q == MOE_QUANT_FP8_BLOCK ? BM : 1];
   __shared__ float lds_amax[4][PHASE == 1 && Q == MOE_QUANT_FP8_BLOCK ? BM : 1];
 
-  const int per = gridDim.x / 8;
-  const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (L >= g.nwg) return;
+  int L;
+  if (!xcd_tile(g, BM, L)) return;  // uniform: no real block for this workgroup
   const int blk = L / g.slices, slice = L % g.slices;
   const int row0 = blk * BM;
-  if (row0 >= *g.num_padded) return;  // uniform: past the last real block
   const int e = g.block_expert[blk];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4;
   const int mylane_row = lane & 15;
@@ -401,12 +412,10 @@ __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
     else return lds_s3;
   };
 
-  const int per = gridDim.x / 8;
-  const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (L >= g.nwg) return;
+  int L;
+  if (!xcd_tile(g, BM, L)) return;  // uniform: no real block for this workgroup
   const int blk = L / g.slices, slice = L % g.slices;
   const int row0 = blk * BM;
-  if (row0 >= *g.num_padded) return;
   const int e = g.block_expert[blk];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4;
   const int lrow = lane & 15;

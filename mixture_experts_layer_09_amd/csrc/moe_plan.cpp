@@ -15,19 +15,25 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 bool quant_is_fp8_act(int q) { return q != MOE_QUANT_BF16; }
 
-// Stream-kernel tiling: fewest K splits that still give enough workgroups to
-// cover the 256 CUs several times over; WT = 4 weight tiles per wave first.
-GemmCfg pick_stream(int64_t blocks_est, int32_t rows, bool need_full_groups) {
-  static const GemmCfg cands[] = {
-      {0, 1, 4, 1, 4}, {0, 1, 4, 2, 4}, {0, 1, 4, 4, 4}, {0, 1, 2, 4, 4}};
-  const int64_t target = 1024;
-  if (need_full_groups) return cands[0];
-  for (const GemmCfg& c : cands) {
-    int64_t rows_per_wg = int64_t(c.waves / c.ksplit) * c.wt * 16;
-    int64_t wgs = blocks_est * ((rows + rows_per_wg - 1) / rows_per_wg);
-    if (wgs >= target) return c;
-  }
-  return cands[3];
+// Decode-sized (16-row block) GEMM shapes, measured on MI355X over the bf16,
+// fp8 and int4 decode workloads: GEMM1 streams fastest as 32 weight rows per
+// workgroup with K split over its four waves, GEMM2 (shorter K) as 64 rows
+// with K split four ways.  The fp8 block-scaled GEMM1 keeps 128 output
+// channels (256 interleaved rows) in one workgroup, since the group maximum
+// of its quantised output spans them.  MOE_STREAM_FORCE_G1 / _G2 pick another
+// shape at build time (index into the table) for tuning builds.
+#ifndef MOE_STREAM_FORCE_G1
+#define MOE_STREAM_FORCE_G1 3
+#endif
+#ifndef MOE_STREAM_FORCE_G2
+#define MOE_STREAM_FORCE_G2 2
+#endif
+const GemmCfg kStreamShapes[] = {
+    {0, 1, 4, 1, 4}, {0, 1, 4, 2, 4}, {0, 1, 4, 4, 4}, {0, 1, 2, 4, 4},
+    {0, 1, 2, 2, 4}, {0, 1, 2, 1, 4}};
+GemmCfg stream_shape(int phase, bool fp8_block) {
+  if (phase == 1) return fp8_block ? kStreamShapes[0] : kStreamShapes[MOE_STREAM_FORCE_G1];
+  return kStreamShapes[MOE_STREAM_FORCE_G2];
 }
 }  // namespace
 
@@ -151,10 +157,9 @@ int make_plan(const moe_problem* p, Plan* plan) {
   q.ksteps_h = p->H / q.kstep;
   q.ksteps_i = p->I / q.kstep;
   q.a2_elem = p->quant == MOE_QUANT_BF16 ? 2 : 1;
-  const int64_t blocks_est = std::max<int64_t>(1, std::min<int64_t>(q.max_blocks, nz));
   if (q.BM == 16) {
-    q.g1 = pick_stream(blocks_est, q.N1, p->quant == MOE_QUANT_FP8_BLOCK);
-    q.g2 = pick_stream(blocks_est, p->H, false);
+    q.g1 = stream_shape(1, p->quant == MOE_QUANT_FP8_BLOCK);
+    q.g2 = stream_shape(2, false);
   } else {
     // fp8 / int4 weights at 128-row blocks: weights and tokens staged in LDS by
     // direct-to-LDS loads, several k-steps in flight
