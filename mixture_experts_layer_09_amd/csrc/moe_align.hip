@@ -372,6 +372,11 @@ hipError_t prologue_q(const moe_problem& p, const PrologueArgs& a, size_t sm,
 }
 }  // namespace
 
+#ifndef MOE_FUSE_QUANT_MAX_PASSES
+#define MOE_FUSE_QUANT_MAX_PASSES 4
+#endif
+constexpr int kFuseQuantMaxPasses = MOE_FUSE_QUANT_MAX_PASSES;
+
 bool prologue_fits(const moe_problem& p, const Plan& q) {
   return q.chunks <= 1 && p.T <= 128 && p.E_routed <= kMaxRouted;
 }
@@ -381,6 +386,16 @@ hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* log
                            uint8_t* xq, float* xs, bool quantise, int32_t* sorted_ids,
                            int32_t* block_expert, int32_t* offsets, int32_t* num_padded,
                            int32_t* scratch, hipStream_t stream) {
+  // The single-workgroup prologue quantises x in passes of one 8-element
+  // group per thread; past a few passes a grid-wide quantisation launch is
+  // faster than the serial loop.
+  const bool fuse_quant =
+      quantise && int64_t(p.T) * p.H <= int64_t(kFuseQuantMaxPasses) * kThreads * 8;
+  if (quantise && !fuse_quant && prologue_fits(p, q)) {
+    hipError_t err = launch_quant_act(p, x, a1, xq, xs, stream);
+    if (err != hipSuccess) return err;
+    quantise = false;
+  }
   if (!prologue_fits(p, q)) {
     hipError_t err = hipSuccess;
     if (logits) err = launch_route(p, logits, ids, w, stream);
