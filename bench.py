@@ -135,6 +135,41 @@ class Pass:
             ev[3].record()
 
 
+KERNEL_SOURCES = ("moe_gemm.hip", "moe_gemm_common.hpp", "moe_device.hpp", "moe_plan.cpp",
+                  "moe_plan.hpp")
+
+
+def kernel_sources_digest():
+    """First 16 hex digits of the SHA-256 over the sources that decide the
+    GEMM kernels and their launch shapes; a stored counter record is only
+    valid while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_09_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(workload_key):
+    """HBM bytes per GEMM1 launch from the committed counter summaries
+    (profiles/traffic_*.md: FETCH_SIZE and WRITE_SIZE per dispatch, each
+    scaled by what the counter reads for a copy of known size), or None when
+    no record covers this workload or the kernel sources changed since."""
+    import glob
+    import re
+    digest = kernel_sources_digest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))):
+        with open(path) as fh:
+            m = re.search(r"```json\s*(\{.*?\})\s*```", fh.read(), re.S)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("bench_workload") == workload_key and rec.get("sources_sha256_16") == digest:
+            return int(rec["traffic_bytes_per_launch"])
+    return None
+
+
 def copy_calibration(mib):
     import torch
     n = mib * 1024 * 1024 // 4
@@ -239,7 +274,8 @@ def main():
                    "tokens": M, "global_batch": M, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "gemm1_act", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_record(args.workload),
                      "algorithmic_bytes_per_launch": int(alg["gemm1_bytes"]),
                      "avg_launch_us": round(float(g1), 2)},
         "layer": {"gpu_ms_per_step": round(gpu_ms, 4), "us_route_align_quant": round(float(pre), 2),
