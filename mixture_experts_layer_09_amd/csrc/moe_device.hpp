@@ -73,7 +73,10 @@ __device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t nib) {
   const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
   // codes of -8,-7,-6,-5 | -4,-3,-2,-1
   const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, sel);
-  const uint32_t m = ((nib >> 3) & 0x01010101u) * 0xFFu;
+  // 0xFF in the bytes whose bit 3 (the sign) is set: per byte 2^8 - 2^0,
+  // written as (t << 5) - (t >> 3) so no carry crosses a byte
+  const uint32_t t = nib & 0x08080808u;
+  const uint32_t m = (t << 5) - (t >> 3);
   return (neg & m) | (pos & ~m);
 }
 

@@ -19,150 +19,15 @@
 //    (block, slice) pairs, slices innermost, so the blocks of one expert --
 //    which share weights -- and the slices of one block -- which share token
 //    rows -- meet in the same L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_device.hpp"
 #include "moe_gemm_common.hpp"
 #include "moe_launch.hpp"
+#include "moe_tile_common.hpp"
 
 namespace moe {
-
-// Epilogue of the tiled kernels, called by every thread of the workgroup:
-// GEMM1 dequantises, applies the activation and stores the half-width rows
-// (fp8-block: per token and 128 channels s = amax / 448 across the waves,
-// through `lds_amax` [4][BM]); GEMM2 dequantises, applies the routing weight
-// and writes the assignments' fp32 rows.
-template <int PHASE, int Q, int ACT, int WT, int NT>
-__device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[WT][NT], int e,
-                                               int row0, int ct, int tile0, bool active,
-                                               float* lds_amax) {
-  constexpr int BM = NT * 16;
-  constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4;
-  const int mylane_row = lane & 15;
-  if (PHASE == 1) {
-    // ---- GEMM1 epilogue: dequantise, activate, store the half-width rows
-    float alpha = 1.f;
-    if (Q == MOE_QUANT_FP8_TENSOR) alpha = g.w_scale[e] * *g.a1;
-    if (Q == MOE_QUANT_W4A8) alpha = *g.a1;
-    constexpr int NV = GATED ? WT / 2 : WT;
-    int cbase[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) cbase[v] = (GATED ? (tile0 / 2 + v) : (tile0 + v)) * 16 + grp * 4;
-    auto act = [&](int c, float (&a)[NV][4]) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (GATED) {
-            a[v][i] = silu(alpha * acc[2 * v][c][i]) * (alpha * acc[2 * v + 1][c][i]);
-          } else {
-            const float h = fmaxf(alpha * acc[v][c][i], 0.f);
-            a[v][i] = h * h;
-          }
-        }
-    };
-    if (Q == MOE_QUANT_FP8_BLOCK) {
-      // per token and 128 channels: s = amax / 448, q = e4m3(a / s)
-      constexpr int CH = NV * 16;    // channels per wave
-      constexpr int WPG = 128 / CH;  // waves per 128-channel group
-#pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        float am = 0.f;
-        if (active && c < ct) {
-          float a[NV][4];
-          act(c, a);
-#pragma unroll
-          for (int v = 0; v < NV; ++v)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(a[v][i]));
-        }
-        am = fmaxf(am, __shfl_xor(am, 16, 64));
-        am = fmaxf(am, __shfl_xor(am, 32, 64));
-        if (grp == 0) lds_amax[wave * BM + c * 16 + mylane_row] = am;
-      }
-      __syncthreads();
-      if (active) {
-        const int w0 = wave - wave % WPG;
-#pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          if (c < ct) {
-            float gm = 0.f;
-#pragma unroll
-            for (int w = 0; w < WPG; ++w) gm = fmaxf(gm, lds_amax[(w0 + w) * BM + c * 16 + mylane_row]);
-            const float s = gm > 0.f ? gm / 448.f : 1.f;
-            float a[NV][4];
-            act(c, a);
-            const int m = row0 + c * 16 + mylane_row;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-              const uint32_t q = e4m3x4(a[v][0] / s, a[v][1] / s, a[v][2] / s, a[v][3] / s);
-              *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) = q;
-            }
-            if (grp == 0 && wave == w0)
-              g.out_scale[size_t(m) * (g.I / 128) + cbase[0] / 128] = s;
-          }
-        }
-      }
-    } else if (active) {
-      const float s2 = (Q == MOE_QUANT_BF16) ? 1.f : *g.a2;
-#pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        if (c < ct) {
-          float a[NV][4];
-          act(c, a);
-          const int m = row0 + c * 16 + mylane_row;
-#pragma unroll
-          for (int v = 0; v < NV; ++v) {
-            if (Q == MOE_QUANT_BF16) {
-              u32x2 o;
-              o[0] = bf16_bits(a[v][0]) | (bf16_bits(a[v][1]) << 16);
-              o[1] = bf16_bits(a[v][2]) | (bf16_bits(a[v][3]) << 16);
-              *reinterpret_cast<u32x2*>(g.out + (size_t(m) * g.I + cbase[v]) * 2) = o;
-            } else {
-              const uint32_t q = e4m3x4(a[v][0] / s2, a[v][1] / s2, a[v][2] / s2, a[v][3] / s2);
-              *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) = q;
-            }
-          }
-        }
-      }
-    }
-  } else {
-    // ---- GEMM2 epilogue: dequantise, weight, write the assignments' rows
-    if (!active) return;
-    float alpha = 1.f;
-    if (Q == MOE_QUANT_FP8_TENSOR) alpha = g.w_scale[e] * *g.a2;
-    if (Q == MOE_QUANT_W4A8) alpha = *g.a2;
-#pragma unroll
-    for (int c = 0; c < NT; ++c) {
-      if (c < ct) {
-        const int m = row0 + c * 16 + mylane_row;
-        const int f = g.sorted_ids[m];
-        if (f < g.A) {
-          const float wgt = alpha * g.topk_w[f];
-#pragma unroll
-          for (int r = 0; r < WT; ++r) {
-            const int n = (tile0 + r) * 16 + grp * 4;
-            *reinterpret_cast<f32x4*>(g.out + (size_t(f) * g.H + n) * 4) = acc[r][c] * wgt;
-          }
-        }
-      }
-    }
-  }
-}
-
-// Workgroup -> tile.  Workgroups are dealt to the 8 XCDs round robin; the
-// tiles of the real blocks (known on the device only) are cut into 8
-// contiguous ranges, one per XCD, so that workgroups sharing a block's token
-// rows or an expert's weights run on one L2.  Workgroups past the real tiles
-// return at once, spread over all XCDs rather than piled on the last one.
-__device__ __forceinline__ bool xcd_tile(const GemmArgs& g, int BM, int& L) {
-  const int nact = min(g.nwg, (*g.num_padded / BM) * g.slices);
-  const int per = (nact + 7) / 8;
-  const int j = blockIdx.x / 8;
-  L = (blockIdx.x % 8) * per + j;
-  return j < per && L < nact;
-}
 
 template <int PHASE, int Q, int ACT, int WT, int NT>
 __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
@@ -357,29 +222,6 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
 // barrier makes all of them visible.  Weight and token fragments are read
 // back with lane-contiguous ds_read_b128 (no bank conflicts).
 
-// Waits until at most N vector-memory operations of this wave are in flight
-// and all its LDS operations are done, then joins the workgroup barrier.  The
-// barrier carries no memory fence: the loads that matter (LDS-DMA of the
-// stage about to be read) are covered by the counted wait, and the loads
-// still in flight for later stages must stay in flight.
-template <int N>
-__device__ __forceinline__ void wait_vm_then_barrier() {
-  // s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (no wait), lgkmcnt 11:8 = 0
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");  // no LDS access moves across the barrier
-}
-
-typedef __attribute__((address_space(1))) const void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-__device__ __forceinline__ void ld_lds16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void ld_lds4(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 4, 0, 0);
-}
-
 template <int Q> struct LdsCfg {
   static constexpr int TILES = 16, NT = 8;  // row tiles / token tiles per workgroup
   static constexpr int A_BYTES = TILES * QT<Q>::FRAG;
@@ -391,7 +233,7 @@ template <int Q> struct LdsCfg {
   static constexpr int LOADS = TILES * QT<Q>::AV / 4 + NT * 2 / 4 + (SC_BYTES ? 1 : 0);
 };
 
-template <int PHASE, int Q, int ACT>
+template <int PHASE, int Q, int ACT, bool PERSIST>
 __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
   using T = QT<Q>;
   using C = LdsCfg<Q>;
@@ -412,60 +254,39 @@ __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
     else return lds_s3;
   };
 
-  int L;
-  if (!xcd_tile(g, BM, L)) return;  // uniform: no real block for this workgroup
-  const int blk = L / g.slices, slice = L % g.slices;
-  const int row0 = blk * BM;
-  const int e = g.block_expert[blk];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4;
-  const int lrow = lane & 15;
+  // one tile: 128 token rows of block L / slices against 256 weight rows
+  auto tile = [&](const int L) {
+    const int blk = L / g.slices, slice = L % g.slices;
+    const int row0 = blk * BM;
+    const int e = g.block_expert[blk];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4;
+    const int lrow = lane & 15;
 
-  const int f_mine = tid < BM ? g.sorted_ids[row0 + tid] : g.A;
-  const int nvalid = __syncthreads_count(tid < BM && f_mine < g.A);
-  const int ct = (nvalid + 15) >> 4;
-  const int wg_tile0 = slice * C::TILES;
-  const int tile0 = wg_tile0 + wave * WT;
-  const bool active = tile0 < g.tiles;
-  const int kblocks = g.K / 128;
-  const int nst = g.K / 128;
+    const int f_mine = tid < BM ? g.sorted_ids[row0 + tid] : g.A;
+    const int nvalid = __syncthreads_count(tid < BM && f_mine < g.A);
+    const int ct = (nvalid + 15) >> 4;
+    const int wg_tile0 = slice * C::TILES;
+    const int tile0 = wg_tile0 + wave * WT;
+    const bool active = tile0 < g.tiles;
+    const int kblocks = g.K / 128;
+    const int nst = g.K / 128;
 
-  // ---- per-lane source addresses, fixed over the stages
-  const size_t ebytes = size_t(g.tiles) * g.steps * T::FRAG;
-  const uint8_t* wexp = g.w + size_t(e) * ebytes;
-  // weight fragments loaded by this wave: tiles wave*4 .. wave*4+3 of the
-  // workgroup (clamped to a real tile past the last one, never computed)
-  const uint8_t* asrc[WT];
-#pragma unroll
-  for (int r = 0; r < WT; ++r) {
-    const int t = min(wg_tile0 + wave * WT + r, g.tiles - 1);
-    asrc[r] = wexp + size_t(t) * g.steps * T::FRAG + lane * 16;
-  }
-  // token fragments loaded by this wave: tiles 2*wave, 2*wave+1
-  uint32_t bsrc[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = (2 * wave + q) * 16 + lrow;
-    int brow;
-    if (PHASE == 1) {
-      const int f = g.sorted_ids[row0 + r];
-      brow = f < g.A ? f / g.Kp : 0;
-    } else {
-      brow = row0 + r;
+    // ---- per-lane source addresses, fixed over the stages
+    const size_t ebytes = size_t(g.tiles) * g.steps * T::FRAG;
+    const uint8_t* wexp = g.w + size_t(e) * ebytes;
+    // weight fragments loaded by this wave: tiles wave*4 .. wave*4+3 of the
+    // workgroup (clamped to a real tile past the last one, never computed)
+    const uint8_t* asrc[WT];
+  #pragma unroll
+    for (int r = 0; r < WT; ++r) {
+      const int t = min(wg_tile0 + wave * WT + r, g.tiles - 1);
+      asrc[r] = wexp + size_t(t) * g.steps * T::FRAG + lane * 16;
     }
-    bsrc[q] = uint32_t(brow) * uint32_t(g.K) + grp * 32;
-  }
-  // scales of a stage: fp8-block weight scales (wave 0 and 3) and token-row
-  // scales (waves 1, 2); W4A8 group scales (every wave loads the same)
-  const float* ssrc = nullptr;
-  int sdst = 0;
-  if (Q == MOE_QUANT_FP8_BLOCK) {
-    if (wave == 0 || wave == 3) {
-      const int t = min(wg_tile0 + (lane & 15), g.tiles - 1);
-      const int rb = PHASE == 1 ? w13_row_block(t, g.I, GATED) : t / 8;
-      ssrc = g.w_scale + (size_t(e) * (g.N / 128) + rb) * kblocks;
-      sdst = 0;
-    } else {
-      const int r = (wave - 1) * 64 + lane;
+    // token fragments loaded by this wave: tiles 2*wave, 2*wave+1
+    uint32_t bsrc[2];
+  #pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = (2 * wave + q) * 16 + lrow;
       int brow;
       if (PHASE == 1) {
         const int f = g.sorted_ids[row0 + r];
@@ -473,136 +294,201 @@ __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
       } else {
         brow = row0 + r;
       }
-      ssrc = g.b_scale + size_t(brow) * kblocks;
-      sdst = 256 + (wave - 1) * 256;
+      bsrc[q] = uint32_t(brow) * uint32_t(g.K) + grp * 32;
     }
-  }
-  if (Q == MOE_QUANT_W4A8) {
-    const int t = min(wg_tile0 + lane / 4, g.tiles - 1);
-    ssrc = g.w_scale + (size_t(e) * g.tiles + t) * g.steps * 16 + (lane % 4) * 4;
-  }
-
-  auto issue = [&](auto bufc, int st) {
-    uint8_t* base = stage_buf(bufc);
-#pragma unroll
-    for (int r = 0; r < WT; ++r)
-#pragma unroll
-      for (int v = 0; v < T::AV; ++v)
-        ld_lds16(asrc[r] + size_t(st) * T::FRAG + v * 1024,
-                   base + (wave * WT + r) * T::FRAG + v * 1024);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        ld_lds16(g.b + bsrc[q] + size_t(st) * 128 + h * 16,
-                   base + C::A_BYTES + (2 * wave + q) * 2048 + h * 1024);
-    if (Q == MOE_QUANT_FP8_BLOCK) ld_lds4(ssrc + st, base + C::A_BYTES + C::B_BYTES + sdst);
-    if (Q == MOE_QUANT_W4A8) ld_lds16(ssrc + size_t(st) * 16, base + C::A_BYTES + C::B_BYTES);
-  };
-
-  f32x4 acc[WT][NT];
-#pragma unroll
-  for (int r = 0; r < WT; ++r)
-#pragma unroll
-    for (int c = 0; c < NT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](auto bufc) {
-    const uint8_t* base = stage_buf(bufc);
-    const float* sc = reinterpret_cast<const float*>(base + C::A_BYTES + C::B_BYTES);
-    i32x8 a8[WT];
-#pragma unroll
-    for (int r = 0; r < WT; ++r) {
-      const uint8_t* ap = base + (wave * WT + r) * T::FRAG + lane * 16;
-      if (Q == MOE_QUANT_W4A8) {
-        a8[r] = int4x32_to_e4m3(*reinterpret_cast<const u32x4*>(ap));
+    // scales of a stage: fp8-block weight scales (wave 0 and 3) and token-row
+    // scales (waves 1, 2); W4A8 group scales (every wave loads the same)
+    const float* ssrc = nullptr;
+    int sdst = 0;
+    if (Q == MOE_QUANT_FP8_BLOCK) {
+      if (wave == 0 || wave == 3) {
+        const int t = min(wg_tile0 + (lane & 15), g.tiles - 1);
+        const int rb = PHASE == 1 ? w13_row_block(t, g.I, GATED) : t / 8;
+        ssrc = g.w_scale + (size_t(e) * (g.N / 128) + rb) * kblocks;
+        sdst = 0;
       } else {
-        a8[r] = fp8_pair(*reinterpret_cast<const u32x4*>(ap),
-                         *reinterpret_cast<const u32x4*>(ap + 1024));
+        const int r = (wave - 1) * 64 + lane;
+        int brow;
+        if (PHASE == 1) {
+          const int f = g.sorted_ids[row0 + r];
+          brow = f < g.A ? f / g.Kp : 0;
+        } else {
+          brow = row0 + r;
+        }
+        ssrc = g.b_scale + size_t(brow) * kblocks;
+        sdst = 256 + (wave - 1) * 256;
       }
     }
-    float ws[WT];
-    f32x4 ws4[WT];
-    if (Q == MOE_QUANT_FP8_BLOCK) {
-#pragma unroll
-      for (int r = 0; r < WT; ++r) ws[r] = sc[wave * WT + r];
-    }
     if (Q == MOE_QUANT_W4A8) {
-#pragma unroll
-      for (int r = 0; r < WT; ++r)
-        ws4[r] = *reinterpret_cast<const f32x4*>(sc + (wave * WT + r) * 16 + grp * 4);
+      const int t = min(wg_tile0 + lane / 4, g.tiles - 1);
+      ssrc = g.w_scale + (size_t(e) * g.tiles + t) * g.steps * 16 + (lane % 4) * 4;
     }
-#pragma unroll
-    for (int c = 0; c < NT; ++c) {
-      if (c < ct) {
-        const uint8_t* bp = base + C::A_BYTES + c * 2048 + lane * 16;
-        const i32x8 bb = fp8_pair(*reinterpret_cast<const u32x4*>(bp),
-                                  *reinterpret_cast<const u32x4*>(bp + 1024));
-        if (Q == MOE_QUANT_FP8_TENSOR) {
-#pragma unroll
-          for (int r = 0; r < WT; ++r) acc[r][c] = mfma_fp8(a8[r], bb, acc[r][c]);
+
+    auto issue = [&](auto bufc, int st) {
+      uint8_t* base = stage_buf(bufc);
+  #pragma unroll
+      for (int r = 0; r < WT; ++r)
+  #pragma unroll
+        for (int v = 0; v < T::AV; ++v)
+          ld_lds16(asrc[r] + size_t(st) * T::FRAG + v * 1024,
+                     base + (wave * WT + r) * T::FRAG + v * 1024);
+  #pragma unroll
+      for (int q = 0; q < 2; ++q)
+  #pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ld_lds16(g.b + bsrc[q] + size_t(st) * 128 + h * 16,
+                     base + C::A_BYTES + (2 * wave + q) * 2048 + h * 1024);
+      if (Q == MOE_QUANT_FP8_BLOCK) ld_lds4(ssrc + st, base + C::A_BYTES + C::B_BYTES + sdst);
+      if (Q == MOE_QUANT_W4A8) ld_lds16(ssrc + size_t(st) * 16, base + C::A_BYTES + C::B_BYTES);
+    };
+
+    f32x4 acc[WT][NT];
+  #pragma unroll
+    for (int r = 0; r < WT; ++r)
+  #pragma unroll
+      for (int c = 0; c < NT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](auto bufc) {
+      const uint8_t* base = stage_buf(bufc);
+      const float* sc = reinterpret_cast<const float*>(base + C::A_BYTES + C::B_BYTES);
+      i32x8 a8[WT];
+  #pragma unroll
+      for (int r = 0; r < WT; ++r) {
+        const uint8_t* ap = base + (wave * WT + r) * T::FRAG + lane * 16;
+        if (Q == MOE_QUANT_W4A8) {
+          a8[r] = int4x32_to_e4m3(*reinterpret_cast<const u32x4*>(ap));
         } else {
-          float bs = 1.f;
-          if (Q == MOE_QUANT_FP8_BLOCK) bs = sc[64 + c * 16 + lrow];
-#pragma unroll
-          for (int r = 0; r < WT; ++r) {
-            const f32x4 t = mfma_fp8(a8[r], bb, f32x4{0.f, 0.f, 0.f, 0.f});
-            if (Q == MOE_QUANT_FP8_BLOCK) {
-              const float s = bs * ws[r];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[r][c][i] = fmaf(t[i], s, acc[r][c][i]);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[r][c][i] = fmaf(t[i], ws4[r][i], acc[r][c][i]);
+          a8[r] = fp8_pair(*reinterpret_cast<const u32x4*>(ap),
+                           *reinterpret_cast<const u32x4*>(ap + 1024));
+        }
+      }
+      float ws[WT];
+      f32x4 ws4[WT];
+      if (Q == MOE_QUANT_FP8_BLOCK) {
+  #pragma unroll
+        for (int r = 0; r < WT; ++r) ws[r] = sc[wave * WT + r];
+      }
+      if (Q == MOE_QUANT_W4A8) {
+  #pragma unroll
+        for (int r = 0; r < WT; ++r)
+          ws4[r] = *reinterpret_cast<const f32x4*>(sc + (wave * WT + r) * 16 + grp * 4);
+      }
+  #pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        if (c < ct) {
+          const uint8_t* bp = base + C::A_BYTES + c * 2048 + lane * 16;
+          const i32x8 bb = fp8_pair(*reinterpret_cast<const u32x4*>(bp),
+                                    *reinterpret_cast<const u32x4*>(bp + 1024));
+          if (Q == MOE_QUANT_FP8_TENSOR) {
+  #pragma unroll
+            for (int r = 0; r < WT; ++r) acc[r][c] = mfma_fp8(a8[r], bb, acc[r][c]);
+          } else {
+            float bs = 1.f;
+            if (Q == MOE_QUANT_FP8_BLOCK) bs = sc[64 + c * 16 + lrow];
+  #pragma unroll
+            for (int r = 0; r < WT; ++r) {
+              const f32x4 t = mfma_fp8(a8[r], bb, f32x4{0.f, 0.f, 0.f, 0.f});
+              if (Q == MOE_QUANT_FP8_BLOCK) {
+                const float s = bs * ws[r];
+  #pragma unroll
+                for (int i = 0; i < 4; ++i) acc[r][c][i] = fmaf(t[i], s, acc[r][c][i]);
+              } else {
+  #pragma unroll
+                for (int i = 0; i < 4; ++i) acc[r][c][i] = fmaf(t[i], ws4[r][i], acc[r][c][i]);
+              }
             }
           }
         }
       }
+    };
+
+    // One pipeline step on buffer B: wait until this wave's loads of stage st
+    // have landed (the S-2 newer stages stay in flight), barrier, refill the
+    // buffer the previous step freed, compute stage st.  Every step issues
+    // exactly one stage of loads -- past the last stage the last one is loaded
+    // again and never read -- so the number of loads in flight is the same on
+    // every path and the counted wait is exact.
+    auto step = [&](auto bufc, int st) {
+      constexpr int B = decltype(bufc)::value;
+      using Refill = std::integral_constant<int, (B + S - 1) % S>;
+      wait_vm_then_barrier<C::LOADS * (S - 2)>();
+      issue(Refill{}, min(st + S - 1, nst - 1));
+      if (active) compute(bufc);
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
+    if constexpr (S > 3) issue(std::integral_constant<int, 2>{}, min(2, nst - 1));
+    // whole rounds of S steps without conditions (a conditional step inside the
+    // loop makes the compiler assume any buffer may hold the newest loads and
+    // wait for all of them), then the remaining steps
+    int st = 0;
+    for (; st + S <= nst; st += S) {
+      step(std::integral_constant<int, 0>{}, st);
+      step(std::integral_constant<int, 1>{}, st + 1);
+      step(std::integral_constant<int, 2>{}, st + 2);
+      if constexpr (S > 3) step(std::integral_constant<int, 3 % S>{}, st + 3);
     }
+    if (st < nst) step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
+    if (S > 3 && st + 2 < nst) step(std::integral_constant<int, 2>{}, st + 2);
+    // drain the surplus loads before the LDS is handed back
+    wait_vm_then_barrier<0>();
+    tiled_epilogue<PHASE, Q, ACT, WT, NT>(g, acc, e, row0, ct, tile0, active, lds_amax);
   };
 
-  // One pipeline step on buffer B: wait until this wave's loads of stage st
-  // have landed (the S-2 newer stages stay in flight), barrier, refill the
-  // buffer the previous step freed, compute stage st.  Every step issues
-  // exactly one stage of loads -- past the last stage the last one is loaded
-  // again and never read -- so the number of loads in flight is the same on
-  // every path and the counted wait is exact.
-  auto step = [&](auto bufc, int st) {
-    constexpr int B = decltype(bufc)::value;
-    using Refill = std::integral_constant<int, (B + S - 1) % S>;
-    wait_vm_then_barrier<C::LOADS * (S - 2)>();
-    issue(Refill{}, min(st + S - 1, nst - 1));
-    if (active) compute(bufc);
-  };
-
-  issue(std::integral_constant<int, 0>{}, 0);
-  issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
-  if constexpr (S > 3) issue(std::integral_constant<int, 2>{}, min(2, nst - 1));
-  // whole rounds of S steps without conditions (a conditional step inside the
-  // loop makes the compiler assume any buffer may hold the newest loads and
-  // wait for all of them), then the remaining steps
-  int st = 0;
-  for (; st + S <= nst; st += S) {
-    step(std::integral_constant<int, 0>{}, st);
-    step(std::integral_constant<int, 1>{}, st + 1);
-    step(std::integral_constant<int, 2>{}, st + 2);
-    if constexpr (S > 3) step(std::integral_constant<int, 3 % S>{}, st + 3);
+  if constexpr (!PERSIST) {
+    int L;
+    if (!xcd_tile(g, BM, L)) return;  // uniform: no real block for this workgroup
+    tile(L);
+  } else {
+    // Persistent: one workgroup per CU, tiles taken in rounds; in round r
+    // the workgroups of XCD x (x = id % 8) take the contiguous tiles
+    // (8r + x)·P + j, so the ones sharing an expert's weights and a block's
+    // token rows start each round together.  Before each tile the previous
+    // tile's stores drain, so the counted waits of the next pipeline see
+    // loads only.
+    const int nact = min(g.nwg, (*g.num_padded / BM) * g.slices);
+    const int P = gridDim.x / 8, x = blockIdx.x % 8, j = blockIdx.x / 8;
+    for (int r = 0;; ++r) {
+      const int L = (r * 8 + x) * P + j;
+      if (L >= nact) break;  // uniform; L grows with r
+      if (r > 0) wait_vm_then_barrier<0>();
+      tile(L);
+    }
   }
-  if (st < nst) step(std::integral_constant<int, 0>{}, st);
-  if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
-  if (S > 3 && st + 2 < nst) step(std::integral_constant<int, 2>{}, st + 2);
-  // drain the surplus loads before the LDS is handed back
-  wait_vm_then_barrier<0>();
-  tiled_epilogue<PHASE, Q, ACT, WT, NT>(g, acc, e, row0, ct, tile0, active, lds_amax);
 }
 
 namespace {
+
+// Workgroups that fit at once when each takes a whole CU, rounded down to a
+// multiple of the 8 XCDs (per device, queried once).
+int persistent_slots() {
+  static int slots[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (slots[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+      cus = 256;
+    slots[dev] = cus / 8 * 8;
+  }
+  return slots[dev];
+}
 
 template <int PHASE, int Q, int ACT>
 hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
   const dim3 grid(unsigned((a.nwg + 7) / 8 * 8)), block(256);
   if constexpr (Q != MOE_QUANT_BF16) {
     if (c.kind == 2) {
-      gemm_lds<PHASE, Q, ACT><<<grid, block, 0, st>>>(a);
+      gemm_lds<PHASE, Q, ACT, false><<<grid, block, 0, st>>>(a);
+      return hipGetLastError();
+    }
+    if (c.kind == 3) {
+      // one workgroup per CU (the stage buffers take most of the LDS)
+      const dim3 pgrid(std::min<unsigned>(grid.x, unsigned(persistent_slots())));
+      gemm_lds<PHASE, Q, ACT, true><<<pgrid, block, 0, st>>>(a);
       return hipGetLastError();
     }
   }

@@ -22,6 +22,9 @@ bool quant_is_fp8_act(int q) { return q != MOE_QUANT_BF16; }
 // channels (256 interleaved rows) in one workgroup, since the group maximum
 // of its quantised output spans them.  MOE_STREAM_FORCE_G1 / _G2 pick another
 // shape at build time (index into the table) for tuning builds.
+#ifndef MOE_LDS_KIND
+#define MOE_LDS_KIND 3
+#endif
 #ifndef MOE_STREAM_FORCE_G1
 #define MOE_STREAM_FORCE_G1 3
 #endif
@@ -162,9 +165,11 @@ int make_plan(const moe_problem* p, Plan* plan) {
     q.g2 = stream_shape(2, false);
   } else {
     // fp8 / int4 weights at 128-row blocks: weights and tokens staged in LDS by
-    // direct-to-LDS loads, several k-steps in flight
+    // direct-to-LDS loads, several k-steps in flight, one persistent
+    // workgroup per CU taking the tiles in rounds (MOE_LDS_KIND 2 at build
+    // time: one workgroup per tile)
     const bool lds = q.BM == 128 && p->quant != MOE_QUANT_BF16;
-    q.g1 = GemmCfg{lds ? 2 : 1, q.BM / 16, 4, 1, 4};
+    q.g1 = GemmCfg{lds ? MOE_LDS_KIND : 1, q.BM / 16, 4, 1, 4};
     q.g2 = q.g1;
   }
 

@@ -22,7 +22,8 @@ constexpr int kTiledMinRows = 48;  // rows per expert from which the tiled GEMMs
 //          A (weights) and B (tokens) fragments loaded straight into registers;
 //  kind 1: tiled kernel, BM tokens staged through LDS and shared by the waves.
 struct GemmCfg {
-  int kind;    // 0 stream, 1 tiled (register-staged weights), 2 tiled LDS-DMA pipeline
+  int kind;    // 0 stream, 1 tiled (register-staged weights), 2 tiled LDS-DMA pipeline,
+               // 3 the same, persistent (one workgroup per CU, tiles in rounds)
   int nt;      // 16-token MFMA tiles per block (BM = 16 * nt)
   int wt;      // 16-row weight tiles per wave
   int ksplit;  // waves of a workgroup that split K (stream kernel)
