@@ -250,7 +250,9 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
 }
 
 // out[t][:] = bf16(sum over valid slots j of y[t*K' + j][:]) with y in fp32,
-// one thread per 8 hidden values.
+// one thread per 8 hidden values.  The rows of up to 8 slots are loaded
+// before any is added, so each thread has 16 loads in flight; the sum still
+// runs in slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
                                                      const float* __restrict__ y,
                                                      uint16_t* __restrict__ out, int T, int H,
@@ -260,16 +262,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   if (i >= int64_t(T) * h8) return;
   const int t = int(i / h8), c = int(i % h8) * 8;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < Kp; ++j) {
-    const int e = ids[size_t(t) * Kp + j];
-    if (e < 0 || e >= E) continue;
-    const float* row = y + (size_t(t) * Kp + j) * H + c;
-    const f32x4 v0 = *reinterpret_cast<const f32x4*>(row);
-    const f32x4 v1 = *reinterpret_cast<const f32x4*>(row + 4);
+  for (int j0 = 0; j0 < Kp; j0 += 8) {
+    f32x4 v[8][2];
+    bool ok[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      s[k] += v0[k];
-      s[4 + k] += v1[k];
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const int e = j < Kp ? ids[size_t(t) * Kp + j] : -1;
+      ok[u] = e >= 0 && e < E;
+      if (ok[u]) {
+        const float* row = y + (size_t(t) * Kp + j) * H + c;
+        v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row));
+        v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (ok[u]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          s[k] += v[u][0][k];
+          s[4 + k] += v[u][1][k];
+        }
+      }
     }
   }
   u32x4 o;
