@@ -18,7 +18,8 @@ Printed: one JSON line.  ``roofline`` relates GEMM1's algorithmic bytes
 half-width intermediate it writes) to its measured time and the 8 TB/s HBM
 peak; ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
 workload on the host cores; ``sweep`` gives every token count of the
-configuration, each pass timed alone after evicting the caches.
+configuration, each pass timed alone after evicting the caches (one
+moe_forward call, and the separate entry points).
 """
 import argparse
 import json
@@ -293,33 +294,46 @@ def main():
 
 
 def sweep(cfg, W, layer):
-    """Each token count of the configuration: passes timed one at a time with
-    the caches evicted (a 512 MiB write) before each, outside the events."""
+    """Each token count of the configuration, timed one pass at a time with
+    the caches evicted (a 512 MiB write) before each, outside the events:
+    `us_median` is one moe_forward call (the library issues its kernels
+    back to back from one host call), `us_components_median` the separate
+    entry points the timed steps above issue from Python."""
     import numpy as np
     import torch
     import synth
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     res = []
+
+    def timed(run, n=10):
+        times = []
+        for _ in range(n):
+            flush.fill_(1.0)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            run()
+            e.record()
+            e.synchronize()
+            times.append(s.elapsed_time(e) * 1e3)
+        return times
+
     for M in cfg.Ms:
         tok = synth.make_tokens(cfg, M)
         x, lg = to_dev(tok["x_bits"]), to_dev(tok["logits"])
         ps = Pass(layer, x, lg, M)
+        out = torch.empty((M, cfg.H), dtype=torch.bfloat16, device="cuda")
+        fwd = lambda: layer.forward(x, lg, out=out)
         for _ in range(3):
             ps.run()
-        times = []
-        for _ in range(10):
-            flush.fill_(1.0)
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            ps.run()
-            e.record()
-            e.synchronize()
-            times.append(s.elapsed_time(e) * 1e3)
+            fwd()
+        comp = timed(ps.run)
+        times = timed(fwd)
         us = float(np.median(times))
         alg = algorithmic(cfg, M, ps.b["topk_ids"].cpu().numpy())
         res.append({"M": M, "us_median": round(us, 2), "us_min": round(float(min(times)), 2),
                     "tokens_per_s": round(M / (us * 1e-6), 1),
                     "hbm_frac": round(alg["layer_bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "us_components_median": round(float(np.median(comp)), 2),
                     "touched_experts": alg["touched"]})
     del flush
     return res

@@ -20,6 +20,7 @@
 //    which share weights -- and the slices of one block -- which share token
 //    rows -- meet in the same L2.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "moe_device.hpp"
@@ -464,17 +465,19 @@ namespace {
 // Workgroups that fit at once when each takes a whole CU, rounded down to a
 // multiple of the 8 XCDs (per device, queried once).
 int persistent_slots() {
-  static int slots[64] = {0};
+  static std::atomic<int> slots[64];  // 0: not queried yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (slots[dev] == 0) {
+  int v = slots[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 8)
       cus = 256;
-    slots[dev] = cus / 8 * 8;
+    v = cus / 8 * 8;
+    slots[dev].store(v, std::memory_order_relaxed);
   }
-  return slots[dev];
+  return v;
 }
 
 template <int PHASE, int Q, int ACT>
