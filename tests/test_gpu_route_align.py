@@ -19,7 +19,9 @@ pytestmark = pytest.mark.gpu
 ROUTE_CASES = [  # T, E_routed, top_k, n_shared, renormalize
     (64, 8, 2, 0, True), (64, 8, 2, 0, False), (1, 128, 8, 0, True), (64, 128, 8, 0, True),
     (16, 512, 10, 1, True), (4096, 512, 10, 1, True), (8192, 20, 8, 0, True),
-    (128, 128, 6, 0, False), (33, 1000, 16, 2, True), (5, 64, 64, 0, True)]
+    (128, 128, 6, 0, False), (33, 1000, 16, 2, True), (5, 64, 64, 0, True),
+    # the limits: 1024 experts in all and K' = 64 slots; one logit per lane x 16
+    (7, 1020, 60, 4, True), (3, 1024, 1, 0, False)]
 
 
 @pytest.mark.parametrize("T,Er,k,ns,renorm", ROUTE_CASES)
@@ -63,7 +65,9 @@ ALIGN_CASES = [  # T, K, E, kind
     (1, 8, 128, "rand"), (64, 2, 8, "rand"), (64, 8, 128, "rand"), (16, 11, 513, "rand"),
     (128, 6, 128, "rand"), (256, 11, 513, "rand"), (4096, 11, 513, "rand"),
     (8192, 8, 20, "rand"), (8192, 6, 128, "rand"), (300, 4, 16, "skew"), (2000, 3, 64, "skew"),
-    (100, 4, 32, "masked"), (3000, 5, 40, "masked"), (127, 3, 3, "rand")]
+    (100, 4, 32, "masked"), (3000, 5, 40, "masked"), (127, 3, 3, "rand"),
+    # no tokens; 1024 experts with exactly one chunk of assignments, and one more
+    (0, 8, 128, "rand"), (1024, 1, 1024, "rand"), (1025, 1, 1024, "rand")]
 
 
 @pytest.mark.parametrize("T,K,E,kind", ALIGN_CASES)
@@ -132,7 +136,8 @@ def test_quant_act_bitexact(quant, T, H):
 RA_CASES = [  # T, E_routed, top_k, n_shared, renormalize, block_m
     (1, 128, 8, 0, True, 0), (64, 128, 8, 0, True, 0), (16, 512, 10, 1, True, 0),
     (64, 8, 2, 0, False, 0), (128, 128, 6, 0, True, 0), (93, 1000, 11, 0, True, 0),
-    (256, 512, 10, 1, True, 0), (4096, 512, 10, 1, True, 0), (8192, 20, 8, 0, True, 0)]
+    (256, 512, 10, 1, True, 0), (4096, 512, 10, 1, True, 0), (8192, 20, 8, 0, True, 0),
+    (2, 1020, 60, 4, True, 0)]
 
 
 @pytest.mark.parametrize("T,Er,k,ns,renorm,bm", RA_CASES)
