@@ -223,28 +223,40 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
 // barrier makes all of them visible.  Weight and token fragments are read
 // back with lane-contiguous ds_read_b128 (no bank conflicts).
 
-template <int Q> struct LdsCfg {
-  static constexpr int TILES = 16, NT = 8;  // row tiles / token tiles per workgroup
+// Workgroup tile of the LDS-staged kernel.  Each of the NWV waves computes
+// 4 weight tiles x 8 token tiles; the waves stand WR along the weight rows
+// and WC along the tokens.  4 waves, WC = 1: 256 weight rows x 128 tokens,
+// three (fp8) or four (int4) stages.  8 waves, WC = 2: 256 x 256, two
+// stages; two waves share each SIMD, so one's LDS reads run under the
+// other's MFMAs, and each weight byte serves twice the tokens.
+template <int Q, int WC, int NWV> struct LdsCfg {
+  static constexpr int WR = NWV / WC;
+  static constexpr int TILES = 4 * WR, NT = 8 * WC;  // weight / token tiles per workgroup
   static constexpr int A_BYTES = TILES * QT<Q>::FRAG;
   static constexpr int B_BYTES = NT * 2048;
   static constexpr int SC_BYTES = (Q == MOE_QUANT_FP8_BLOCK || Q == MOE_QUANT_W4A8) ? 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
-  static constexpr int S = Q == MOE_QUANT_W4A8 ? 4 : 3;   // stages in flight
+  static constexpr int S = NWV == 8 ? 2 : (Q == MOE_QUANT_W4A8 ? 4 : 3);  // stages in flight
   // loads per wave per stage: weight fragments, token fragments, scales
-  static constexpr int LOADS = TILES * QT<Q>::AV / 4 + NT * 2 / 4 + (SC_BYTES ? 1 : 0);
+  static constexpr int LOADS = TILES * QT<Q>::AV / NWV + NT * 2 / NWV + (SC_BYTES ? 1 : 0);
+  static_assert(S * STAGE <= 160 * 1024 - 4096, "stage buffers exceed the LDS");
+  static_assert(Q != MOE_QUANT_FP8_BLOCK || WC == 1,
+                "block scales: one workgroup spans the 128 output channels of a group");
+  static_assert(TILES % NWV == 0 && NT % NWV == 0, "whole fragments per wave");
 };
 
-template <int PHASE, int Q, int ACT, bool PERSIST>
-__global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
+template <int PHASE, int Q, int ACT, int WC, int NWV, bool PERSIST>
+__global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
   using T = QT<Q>;
-  using C = LdsCfg<Q>;
-  constexpr int WT = 4, NT = C::NT, BM = NT * 16, S = C::S;
+  using C = LdsCfg<Q, WC, NWV>;
+  // WT x NW: one wave's weight tiles x token tiles; BM: token rows of the workgroup
+  constexpr int WT = 4, NW = 8, NT = C::NT, BM = NT * 16, S = C::S, WR = C::WR;
   constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
   // one array per stage: the compiler then sees that a stage's LDS reads do
   // not alias the LDS-DMA writes into the other stages and does not wait for them
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[S > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[S > 3 ? C::STAGE : 16];
   __shared__ float lds_amax[PHASE == 1 && Q == MOE_QUANT_FP8_BLOCK ? 4 * BM : 1];
   auto stage_buf = [&](auto bufc) -> uint8_t* {
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
     else return lds_s3;
   };
 
-  // one tile: 128 token rows of block L / slices against 256 weight rows
+  // one tile: the BM token rows of block L / slices against 16 * TILES weight rows
   auto tile = [&](const int L) {
     const int blk = L / g.slices, slice = L % g.slices;
     const int row0 = blk * BM;
@@ -263,31 +275,35 @@ __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4;
     const int lrow = lane & 15;
 
+    // this wave's weight / token group (constants when the waves stand in a row)
+    const int wr = WC == 1 ? wave : wave % WR, wc = WC == 1 ? 0 : wave / WR;
     const int f_mine = tid < BM ? g.sorted_ids[row0 + tid] : g.A;
     const int nvalid = __syncthreads_count(tid < BM && f_mine < g.A);
-    const int ct = (nvalid + 15) >> 4;
+    // token tiles holding rows, counted within this wave's group
+    const int ct = min(max(((nvalid + 15) >> 4) - wc * NW, 0), NW);
     const int wg_tile0 = slice * C::TILES;
-    const int tile0 = wg_tile0 + wave * WT;
-    const bool active = tile0 < g.tiles;
+    const int tile0 = wg_tile0 + wr * WT;
+    const bool active = tile0 < g.tiles && ct > 0;
     const int kblocks = g.K / 128;
     const int nst = g.K / 128;
 
     // ---- per-lane source addresses, fixed over the stages
     const size_t ebytes = size_t(g.tiles) * g.steps * T::FRAG;
     const uint8_t* wexp = g.w + size_t(e) * ebytes;
-    // weight fragments loaded by this wave: tiles wave*4 .. wave*4+3 of the
-    // workgroup (clamped to a real tile past the last one, never computed)
-    const uint8_t* asrc[WT];
+    // weight fragments loaded into LDS by this wave: tiles wave*LA ..
+    // wave*LA+LA-1 of the workgroup (clamped to a real tile past the last
+    // one, never computed); token tiles wave*LB .. wave*LB+LB-1
+    constexpr int LA = C::TILES / NWV, LB = NT / NWV;
+    const uint8_t* asrc[LA];
   #pragma unroll
-    for (int r = 0; r < WT; ++r) {
-      const int t = min(wg_tile0 + wave * WT + r, g.tiles - 1);
+    for (int r = 0; r < LA; ++r) {
+      const int t = min(wg_tile0 + wave * LA + r, g.tiles - 1);
       asrc[r] = wexp + size_t(t) * g.steps * T::FRAG + lane * 16;
     }
-    // token fragments loaded by this wave: tiles 2*wave, 2*wave+1
-    uint32_t bsrc[2];
+    uint32_t bsrc[LB];
   #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = (2 * wave + q) * 16 + lrow;
+    for (int q = 0; q < LB; ++q) {
+      const int r = (LB * wave + q) * 16 + lrow;
       int brow;
       if (PHASE == 1) {
         const int f = g.sorted_ids[row0 + r];
@@ -328,58 +344,63 @@ __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
     auto issue = [&](auto bufc, int st) {
       uint8_t* base = stage_buf(bufc);
   #pragma unroll
-      for (int r = 0; r < WT; ++r)
+      for (int r = 0; r < LA; ++r)
   #pragma unroll
         for (int v = 0; v < T::AV; ++v)
           ld_lds16(asrc[r] + size_t(st) * T::FRAG + v * 1024,
-                     base + (wave * WT + r) * T::FRAG + v * 1024);
+                     base + (wave * LA + r) * T::FRAG + v * 1024);
   #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < LB; ++q)
   #pragma unroll
         for (int h = 0; h < 2; ++h)
           ld_lds16(g.b + bsrc[q] + size_t(st) * 128 + h * 16,
-                     base + C::A_BYTES + (2 * wave + q) * 2048 + h * 1024);
+                     base + C::A_BYTES + (LB * wave + q) * 2048 + h * 1024);
       if (Q == MOE_QUANT_FP8_BLOCK) ld_lds4(ssrc + st, base + C::A_BYTES + C::B_BYTES + sdst);
       if (Q == MOE_QUANT_W4A8) ld_lds16(ssrc + size_t(st) * 16, base + C::A_BYTES + C::B_BYTES);
     };
 
-    f32x4 acc[WT][NT];
+    f32x4 acc[WT][NW];
   #pragma unroll
     for (int r = 0; r < WT; ++r)
   #pragma unroll
-      for (int c = 0; c < NT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NW; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // byte offsets of this lane's fragments in a stage.  Every LDS read below
+    // indexes the stage array once with a whole offset: a longer chain of
+    // pointer steps hides from the compiler which array a read touches, and
+    // it then waits for every direct-to-LDS load in flight before the read.
+    const int a_off = wr * WT * T::FRAG + lane * 16;
+    const int b_off = C::A_BYTES + wc * NW * 2048 + lane * 16;
+    auto rd16 = [](const uint8_t* base, int off) {
+      return *reinterpret_cast<const u32x4*>(base + off);
+    };
     auto compute = [&](auto bufc) {
       const uint8_t* base = stage_buf(bufc);
       const float* sc = reinterpret_cast<const float*>(base + C::A_BYTES + C::B_BYTES);
       i32x8 a8[WT];
   #pragma unroll
       for (int r = 0; r < WT; ++r) {
-        const uint8_t* ap = base + (wave * WT + r) * T::FRAG + lane * 16;
         if (Q == MOE_QUANT_W4A8) {
-          a8[r] = int4x32_to_e4m3(*reinterpret_cast<const u32x4*>(ap));
+          a8[r] = int4x32_to_e4m3(rd16(base, a_off + r * T::FRAG));
         } else {
-          a8[r] = fp8_pair(*reinterpret_cast<const u32x4*>(ap),
-                           *reinterpret_cast<const u32x4*>(ap + 1024));
+          a8[r] = fp8_pair(rd16(base, a_off + r * T::FRAG), rd16(base, a_off + r * T::FRAG + 1024));
         }
       }
       float ws[WT];
       f32x4 ws4[WT];
       if (Q == MOE_QUANT_FP8_BLOCK) {
   #pragma unroll
-        for (int r = 0; r < WT; ++r) ws[r] = sc[wave * WT + r];
+        for (int r = 0; r < WT; ++r) ws[r] = sc[wr * WT + r];
       }
       if (Q == MOE_QUANT_W4A8) {
   #pragma unroll
         for (int r = 0; r < WT; ++r)
-          ws4[r] = *reinterpret_cast<const f32x4*>(sc + (wave * WT + r) * 16 + grp * 4);
+          ws4[r] = *reinterpret_cast<const f32x4*>(sc + (wr * WT + r) * 16 + grp * 4);
       }
   #pragma unroll
-      for (int c = 0; c < NT; ++c) {
+      for (int c = 0; c < NW; ++c) {
         if (c < ct) {
-          const uint8_t* bp = base + C::A_BYTES + c * 2048 + lane * 16;
-          const i32x8 bb = fp8_pair(*reinterpret_cast<const u32x4*>(bp),
-                                    *reinterpret_cast<const u32x4*>(bp + 1024));
+          const i32x8 bb = fp8_pair(rd16(base, b_off + c * 2048), rd16(base, b_off + c * 2048 + 1024));
           if (Q == MOE_QUANT_FP8_TENSOR) {
   #pragma unroll
             for (int r = 0; r < WT; ++r) acc[r][c] = mfma_fp8(a8[r], bb, acc[r][c]);
@@ -417,8 +438,9 @@ __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
       if (active) compute(bufc);
     };
 
+    // the first S - 1 stages
     issue(std::integral_constant<int, 0>{}, 0);
-    issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
+    if constexpr (S > 2) issue(std::integral_constant<int, 1>{}, min(1, nst - 1));
     if constexpr (S > 3) issue(std::integral_constant<int, 2>{}, min(2, nst - 1));
     // whole rounds of S steps without conditions (a conditional step inside the
     // loop makes the compiler assume any buffer may hold the newest loads and
@@ -427,15 +449,16 @@ __global__ __launch_bounds__(256, 1) void gemm_lds(GemmArgs g) {
     for (; st + S <= nst; st += S) {
       step(std::integral_constant<int, 0>{}, st);
       step(std::integral_constant<int, 1>{}, st + 1);
-      step(std::integral_constant<int, 2>{}, st + 2);
+      if constexpr (S > 2) step(std::integral_constant<int, 2>{}, st + 2);
       if constexpr (S > 3) step(std::integral_constant<int, 3 % S>{}, st + 3);
     }
     if (st < nst) step(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
-    if (S > 3 && st + 2 < nst) step(std::integral_constant<int, 2>{}, st + 2);
+    if (S > 2 && st + 1 < nst) step(std::integral_constant<int, 1 % S>{}, st + 1);
+    if (S > 3 && st + 2 < nst) step(std::integral_constant<int, 2 % S>{}, st + 2);
     // drain the surplus loads before the LDS is handed back
     wait_vm_then_barrier<0>();
-    tiled_epilogue<PHASE, Q, ACT, WT, NT>(g, acc, e, row0, ct, tile0, active, lds_amax);
+    tiled_epilogue<PHASE, Q, ACT, WT, NW>(g, acc, e, row0 + wc * NW * 16, ct, tile0, active,
+                                          lds_amax);
   };
 
   if constexpr (!PERSIST) {
@@ -484,21 +507,24 @@ template <int PHASE, int Q, int ACT>
 hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
   const dim3 grid(unsigned((a.nwg + 7) / 8 * 8)), block(256);
   if constexpr (Q != MOE_QUANT_BF16) {
-    if (c.kind == 2) {
-      gemm_lds<PHASE, Q, ACT, false><<<grid, block, 0, st>>>(a);
-      return hipGetLastError();
-    }
-    if (c.kind == 3) {
-      // one workgroup per CU (the stage buffers take most of the LDS)
-      const dim3 pgrid(std::min<unsigned>(grid.x, unsigned(persistent_slots())));
-      gemm_lds<PHASE, Q, ACT, true><<<pgrid, block, 0, st>>>(a);
-      return hipGetLastError();
-    }
-  }
-  if constexpr (Q == MOE_QUANT_FP8_TENSOR) {
-    if (c.nt == 16) {
-      gemm_tiled<PHASE, Q, ACT, 4, 16><<<grid, block, 0, st>>>(a);
-      return hipGetLastError();
+    if (c.kind == 2 || c.kind == 3) {
+      // kind 3: one workgroup per CU (the stage buffers take most of the LDS)
+      const dim3 pgrid(c.kind == 3 ? std::min<unsigned>(grid.x, unsigned(persistent_slots()))
+                                   : grid.x);
+      if (c.nt == 8) {
+        if (c.kind == 3) gemm_lds<PHASE, Q, ACT, 1, 4, true><<<pgrid, block, 0, st>>>(a);
+        else gemm_lds<PHASE, Q, ACT, 1, 4, false><<<pgrid, block, 0, st>>>(a);
+        return hipGetLastError();
+      }
+      if constexpr (Q == MOE_QUANT_FP8_TENSOR) {
+        // 8 waves, 256 x 256: one workgroup per tile (the int4 unpacking and
+        // the persistent loop's state do not fit the registers of 8 waves)
+        if (c.nt == 16 && c.kind == 2) {
+          gemm_lds<PHASE, Q, ACT, 2, 8, false><<<grid, dim3(512), 0, st>>>(a);
+          return hipGetLastError();
+        }
+      }
+      return hipErrorInvalidValue;
     }
   }
   if (c.nt == 8) gemm_tiled<PHASE, Q, ACT, 4, 8><<<grid, block, 0, st>>>(a);

@@ -22,6 +22,9 @@ bool quant_is_fp8_act(int q) { return q != MOE_QUANT_BF16; }
 // channels (256 interleaved rows) in one workgroup, since the group maximum
 // of its quantised output spans them.  MOE_STREAM_FORCE_G1 / _G2 pick another
 // shape at build time (index into the table) for tuning builds.
+#ifndef MOE_WIDE_MIN_ROWS
+#define MOE_WIDE_MIN_ROWS 256
+#endif
 #ifndef MOE_LDS_KIND
 #define MOE_LDS_KIND 3
 #endif
@@ -136,16 +139,21 @@ int make_plan(const moe_problem* p, Plan* plan) {
   // ---- tile table: the alignment block follows the expected rows per
   // expert.  Decode-sized problems stream weights 16 token rows at a time;
   // with many rows per expert the tiled kernels stage 128 token rows in LDS
-  // and reuse every weight fragment across them.
+  // and reuse every weight fragment across them; fp8 per-tensor weights with
+  // 256 or more rows per expert take 256 token rows per block, so that each
+  // weight byte brought into the LDS serves twice the tokens.
   const int64_t rows_per_expert = q.A / std::max(1, p->E);
+  const bool wide_ok = p->quant == MOE_QUANT_FP8_TENSOR;
   if (p->block_m != 0) {
     q.BM = p->block_m;
+  } else if (rows_per_expert >= MOE_WIDE_MIN_ROWS && wide_ok) {
+    q.BM = 256;
   } else if (rows_per_expert >= kTiledMinRows) {
     q.BM = 128;
   } else {
     q.BM = 16;
   }
-  if (q.BM == 256 && p->quant != MOE_QUANT_FP8_TENSOR)
+  if (q.BM == 256 && !wide_ok)
     return fail(MOE_ERR_UNSUPPORTED, "block_m = 256 runs for the fp8 per-tensor mode only");
   const int64_t nz = std::min<int64_t>(p->E, q.A);
   q.max_blocks = std::min<int64_t>(q.A, (q.A + nz * (q.BM - 1)) / q.BM);
@@ -167,9 +175,10 @@ int make_plan(const moe_problem* p, Plan* plan) {
     // fp8 / int4 weights at 128-row blocks: weights and tokens staged in LDS by
     // direct-to-LDS loads, several k-steps in flight, one persistent
     // workgroup per CU taking the tiles in rounds (MOE_LDS_KIND 2 at build
-    // time: one workgroup per tile)
-    const bool lds = q.BM == 128 && p->quant != MOE_QUANT_BF16;
-    q.g1 = GemmCfg{lds ? MOE_LDS_KIND : 1, q.BM / 16, 4, 1, 4};
+    // time: one workgroup per tile).  256-row blocks: 8 waves, one workgroup
+    // per tile.
+    const bool lds = q.BM >= 128 && p->quant != MOE_QUANT_BF16;
+    q.g1 = GemmCfg{lds ? (q.BM == 256 ? 2 : MOE_LDS_KIND) : 1, q.BM / 16, 4, 1, 4};
     q.g2 = q.g1;
   }
 

@@ -180,7 +180,8 @@ def test_invalid_call_enqueues_nothing():
 
 
 TILED = [(q, a, bm) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
-         for a in ("silu", "relu2") for bm in (64, 128)]
+         for a in ("silu", "relu2") for bm in (64, 128)] + \
+        [("fp8_tensor", a, 256) for a in ("silu", "relu2")]
 
 
 @pytest.mark.parametrize("quant,act,bm", TILED)
@@ -200,3 +201,22 @@ def test_forward_tiled_ragged(quant, act, bm):
     torch.cuda.synchronize()
     ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"], sc["a1"], sc["a2"])
     assert_close(out.float().cpu().numpy(), ref, quant, f"tiled {quant} {act} bm={bm}")
+
+
+@pytest.mark.parametrize("act", ["silu", "relu2"])
+def test_forward_wide_blocks_by_default(act):
+    """fp8 per-tensor with 256+ rows per expert takes 256-row blocks by
+    itself: several full blocks per expert, ragged last blocks, and blocks
+    whose second half of token tiles is empty or partly filled."""
+    cfg = ad_hoc(94, "fp8_tensor", act, H=512, I=384, E_routed=4, top_k=2, n_shared=1)
+    say(f"wide fp8_tensor {act}")
+    W = synth.make_weights(cfg, seed=779)
+    T = 700
+    tok = synth.make_tokens(cfg, T, seed=80)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
+    assert moe.block_m(layer.problem(T)) == 256
+    out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
+    torch.cuda.synchronize()
+    ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"], sc["a1"], sc["a2"])
+    assert_close(out.float().cpu().numpy(), ref, "fp8_tensor", f"wide {act}")
