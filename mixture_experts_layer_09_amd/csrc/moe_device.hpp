@@ -94,8 +94,13 @@ __device__ __forceinline__ i32x8 int4x32_to_e4m3(const u32x4& v) {
 }
 
 // ---------------------------------------------------------------- math
-// SiLU from its definition, g * sigmoid(g), in fp32.
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// SiLU from its definition, g * sigmoid(g), in fp32 with the hardware base-2
+// exponential and reciprocal (each within about one ulp): e^-g = 2^(-g log2 e).
+// Large negative g gives 2^+inf = inf, reciprocal 0, result -0; large positive
+// g gives 2^-inf = 0 and g itself.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
 
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_max(float v) {

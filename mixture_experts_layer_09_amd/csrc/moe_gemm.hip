@@ -217,19 +217,20 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
       for (int w = 0; w < WPG; ++w) gm = fmaxf(gm, amax_s[w0 + w][lane & 15]);
       const float s = gm > 0.f ? gm / 448.f : 1.f;
       if (active) {
+        const float rs = 1.f / s;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const uint32_t q = e4m3x4(a[v][0] / s, a[v][1] / s, a[v][2] / s, a[v][3] / s);
+          const uint32_t q = e4m3x4(a[v][0] * rs, a[v][1] * rs, a[v][2] * rs, a[v][3] * rs);
           *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) = q;
         }
         if (grp == 0 && wave == w0) g.out_scale[size_t(m) * (g.I / 128) + cbase[0] / 128] = s;
       }
     } else {
       if (active) {
-        const float s2 = *g.a2;
+        const float rs2 = 1.f / *g.a2;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const uint32_t q = e4m3x4(a[v][0] / s2, a[v][1] / s2, a[v][2] / s2, a[v][3] / s2);
+          const uint32_t q = e4m3x4(a[v][0] * rs2, a[v][1] * rs2, a[v][2] * rs2, a[v][3] * rs2);
           *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) = q;
         }
       }

@@ -72,12 +72,13 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
 #pragma unroll
             for (int w = 0; w < WPG; ++w) gm = fmaxf(gm, lds_amax[(w0 + w) * BM + c * 16 + mylane_row]);
             const float s = gm > 0.f ? gm / 448.f : 1.f;
+            const float rs = 1.f / s;
             float a[NV][4];
             act(c, a);
             const int m = row0 + c * 16 + mylane_row;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-              const uint32_t q = e4m3x4(a[v][0] / s, a[v][1] / s, a[v][2] / s, a[v][3] / s);
+              const uint32_t q = e4m3x4(a[v][0] * rs, a[v][1] * rs, a[v][2] * rs, a[v][3] * rs);
               *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) = q;
             }
             if (grp == 0 && wave == w0)
@@ -86,7 +87,8 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
         }
       }
     } else if (active) {
-      const float s2 = (Q == MOE_QUANT_BF16) ? 1.f : *g.a2;
+      // quotients by the intermediate scale as products with its reciprocal
+      const float rs2 = (Q == MOE_QUANT_BF16) ? 1.f : 1.f / *g.a2;
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         if (c < ct) {
@@ -101,7 +103,7 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
               o[1] = bf16_bits(a[v][2]) | (bf16_bits(a[v][3]) << 16);
               *reinterpret_cast<u32x2*>(g.out + (size_t(m) * g.I + cbase[v]) * 2) = o;
             } else {
-              const uint32_t q = e4m3x4(a[v][0] / s2, a[v][1] / s2, a[v][2] / s2, a[v][3] / s2);
+              const uint32_t q = e4m3x4(a[v][0] * rs2, a[v][1] * rs2, a[v][2] * rs2, a[v][3] * rs2);
               *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) = q;
             }
           }
