@@ -245,6 +245,66 @@ template <int Q, int WC, int NWV> struct LdsCfg {
   static_assert(TILES % NWV == 0 && NT % NWV == 0, "whole fragments per wave");
 };
 
+// GEMM1 epilogue of the 8-wave fp8 per-tensor tile through the LDS: each
+// wave writes its e4m3 outputs (4 channels of one token per lane and MFMA
+// tile) into a row-major [token][channel] copy of the workgroup's output
+// tile -- rows 0-127 in s0, 128-255 in s1, rows padded by 16 bytes so the 16
+// tokens of one store fall in distinct banks -- and the workgroup then
+// writes whole rows (256 or 128 bytes) with 16 bytes per lane, instead of
+// 16 rows x 16 bytes per store.
+template <int ACT, int WT, int NW>
+__device__ __forceinline__ void lds_epilogue1(const GemmArgs& g, const f32x4 (&acc)[WT][NW],
+                                              int e, int row0, int wr, int wc, int ct,
+                                              int ct_all, int wg_tile0, bool active,
+                                              uint8_t* s0, uint8_t* s1) {
+  constexpr bool GATED = ACT == MOE_ACT_SILU_GATED;
+  constexpr int NV = GATED ? WT / 2 : WT;  // 4-channel vectors per lane and token tile
+  constexpr int OC = GATED ? 128 : 256;    // output channels (bytes) of the workgroup tile
+  constexpr int OCP = OC + 16;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, lrow = lane & 15;
+  if (active) {
+    const float alpha = g.w_scale[e] * *g.a1;
+    const float rs2 = 1.f / *g.a2;
+    uint8_t* ob = wc == 0 ? s0 : s1;
+#pragma unroll
+    for (int c = 0; c < NW; ++c) {
+      if (c < ct) {
+        uint8_t* orow = ob + (c * 16 + lrow) * OCP + grp * 4;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          float a[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (GATED) {
+              a[i] = silu(alpha * acc[2 * v][c][i]) * (alpha * acc[2 * v + 1][c][i]);
+            } else {
+              const float h = fmaxf(alpha * acc[v][c][i], 0.f);
+              a[i] = h * h;
+            }
+          }
+          *reinterpret_cast<uint32_t*>(orow + (wr * NV + v) * 16) =
+              e4m3x4(a[0] * rs2, a[1] * rs2, a[2] * rs2, a[3] * rs2);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // whole rows out: the rows of the token tiles holding real rows, the
+  // channels of the real weight tiles
+  const int col0 = (GATED ? wg_tile0 / 2 : wg_tile0) * 16;
+  const int ncols = min(OC, g.I - col0);
+  const int nrows = ct_all * 16;
+  constexpr int LPR = OC / 16, RPP = 512 / LPR;  // lanes per row, rows per pass
+  const int ch = (threadIdx.x % LPR) * 16;
+  if (ch < ncols) {
+    for (int r = threadIdx.x / LPR; r < nrows; r += RPP) {
+      const uint8_t* src = (r < 128 ? s0 : s1) + (r & 127) * OCP + ch;
+      *reinterpret_cast<u32x4*>(g.out + size_t(row0 + r) * g.I + col0 + ch) =
+          *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+}
+
 template <int PHASE, int Q, int ACT, int WC, int NWV, bool PERSIST>
 __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
   using T = QT<Q>;
@@ -457,8 +517,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
     if (S > 3 && st + 2 < nst) step(std::integral_constant<int, 2 % S>{}, st + 2);
     // drain the surplus loads before the LDS is handed back
     wait_vm_then_barrier<0>();
-    tiled_epilogue<PHASE, Q, ACT, WT, NW>(g, acc, e, row0 + wc * NW * 16, ct, tile0, active,
-                                          lds_amax);
+    if constexpr (NWV == 8 && PHASE == 1) {
+      static_assert(Q == MOE_QUANT_FP8_TENSOR && C::STAGE >= 128 * (256 + 16), "8-wave GEMM1 tile");
+      lds_epilogue1<ACT, WT, NW>(g, acc, e, row0, wr, wc, ct, (nvalid + 15) >> 4, wg_tile0,
+                                 active, lds_s0, lds_s1);
+    } else {
+      tiled_epilogue<PHASE, Q, ACT, WT, NW>(g, acc, e, row0 + wc * NW * 16, ct, tile0, active,
+                                            lds_amax);
+    }
   };
 
   if constexpr (!PERSIST) {
