@@ -116,18 +116,23 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
     float alpha = 1.f;
     if (Q == MOE_QUANT_FP8_TENSOR) alpha = g.w_scale[e] * *g.a2;
     if (Q == MOE_QUANT_W4A8) alpha = *g.a2;
+    // the rows' assignment indices and routing weights first, all loads in
+    // flight together (every row of the block exists; padding reads weight 0)
+    int fs[NT];
+    float ws[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) fs[c] = g.sorted_ids[row0 + c * 16 + mylane_row];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) ws[c] = g.topk_w[fs[c] < g.A ? fs[c] : 0];
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-      if (c < ct) {
-        const int m = row0 + c * 16 + mylane_row;
-        const int f = g.sorted_ids[m];
-        if (f < g.A) {
-          const float wgt = alpha * g.topk_w[f];
+      const int f = fs[c];
+      if (c < ct && f < g.A) {
+        const float wgt = alpha * ws[c];
 #pragma unroll
-          for (int r = 0; r < WT; ++r) {
-            const int n = (tile0 + r) * 16 + grp * 4;
-            *reinterpret_cast<f32x4*>(g.out + (size_t(f) * g.H + n) * 4) = acc[r][c] * wgt;
-          }
+        for (int r = 0; r < WT; ++r) {
+          const int n = (tile0 + r) * 16 + grp * 4;
+          *reinterpret_cast<f32x4*>(g.out + (size_t(f) * g.H + n) * 4) = acc[r][c] * wgt;
         }
       }
     }
