@@ -100,12 +100,12 @@ def test_components_equal_forward():
     assert torch.equal(out.view(torch.int16), b2["out"].view(torch.int16))
 
 
-@pytest.mark.parametrize("quant", ["bf16", "fp8_block"])
-def test_prerouted_with_masked_slots(quant):
+@pytest.mark.parametrize("quant,T", [("bf16", 29), ("fp8_block", 29), ("bf16", 13),
+                                     ("fp8_block", 13)])
+def test_prerouted_with_masked_slots(quant, T):
     """Routing supplied by the caller; ids outside [0, E) contribute nothing."""
     cfg = ad_hoc(91, quant, "silu", H=256, I=256, E_routed=12, top_k=4)
     W = synth.make_weights(cfg, seed=99)
-    T = 29
     tok = synth.make_tokens(cfg, T, seed=5)
     rng = np.random.default_rng(6)
     ids = rng.integers(0, 12, (T, 4)).astype(np.int32)

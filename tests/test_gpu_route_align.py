@@ -137,7 +137,10 @@ RA_CASES = [  # T, E_routed, top_k, n_shared, renormalize, block_m
     (1, 128, 8, 0, True, 0), (64, 128, 8, 0, True, 0), (16, 512, 10, 1, True, 0),
     (64, 8, 2, 0, False, 0), (128, 128, 6, 0, True, 0), (93, 1000, 11, 0, True, 0),
     (256, 512, 10, 1, True, 0), (4096, 512, 10, 1, True, 0), (8192, 20, 8, 0, True, 0),
-    (2, 1020, 60, 4, True, 0)]
+    (2, 1020, 60, 4, True, 0),
+    # small batches: both routing layouts, 64 slots per token, explicit blocks
+    (8, 128, 8, 0, True, 0), (3, 1000, 11, 2, False, 0), (1, 1020, 60, 4, True, 0),
+    (5, 8, 2, 0, True, 16), (21, 40, 3, 0, False, 64)]
 
 
 @pytest.mark.parametrize("T,Er,k,ns,renorm,bm", RA_CASES)
@@ -177,7 +180,9 @@ def test_prepare_route_align_bitexact(T, Er, k, ns, renorm, bm):
                                                ("fp8_tensor", 1, 4096, 128, 6, 0),
                                                ("fp8_tensor", 128, 4096, 128, 6, 0),
                                                ("w4a8", 64, 6144, 20, 8, 0),
-                                               ("fp8_block", 300, 2048, 512, 10, 1)])
+                                               ("fp8_block", 300, 2048, 512, 10, 1),
+                                               ("fp8_block", 4, 2048, 512, 10, 1),
+                                               ("w4a8", 8, 6144, 20, 8, 0)])
 def test_prepare_quantise_equals_separate_calls(quant, T, H, Er, k, ns):
     """moe_prepare's fused routing + quantisation + alignment is bit-identical
     to moe_route, moe_quant_act and moe_align called one after another."""
