@@ -224,19 +224,22 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
 // back with lane-contiguous ds_read_b128 (no bank conflicts).
 
 // Workgroup tile of the LDS-staged kernel.  Each of the NWV waves computes
-// 4 weight tiles x 8 token tiles; the waves stand WR along the weight rows
-// and WC along the tokens.  4 waves, WC = 1: 256 weight rows x 128 tokens,
-// three (fp8) or four (int4) stages.  8 waves, WC = 2: 256 x 256, two
-// stages; two waves share each SIMD, so one's LDS reads run under the
-// other's MFMAs, and each weight byte serves twice the tokens.
-template <int Q, int WC, int NWV> struct LdsCfg {
+// WT weight tiles x 8 token tiles; the waves stand WR along the weight rows
+// and WC along the tokens.  4 waves of 4 tiles, WC = 1: 256 weight rows x
+// 128 tokens, three (fp8) or four (int4) stages.  8 waves of 2 tiles,
+// WC = 1: the same 256 x 128 with two waves per SIMD (int4, fp8 block
+// scales: one wave's conversions and scale FMAs run under the other's
+// MFMAs).  8 waves of 4 tiles, WC = 2: 256 x 256, two stages; one wave's
+// LDS reads run under the other's MFMAs, and each weight byte serves twice
+// the tokens.
+template <int Q, int WC, int NWV, int WT = 4> struct LdsCfg {
   static constexpr int WR = NWV / WC;
-  static constexpr int TILES = 4 * WR, NT = 8 * WC;  // weight / token tiles per workgroup
+  static constexpr int TILES = WT * WR, NT = 8 * WC;  // weight / token tiles per workgroup
   static constexpr int A_BYTES = TILES * QT<Q>::FRAG;
   static constexpr int B_BYTES = NT * 2048;
   static constexpr int SC_BYTES = (Q == MOE_QUANT_FP8_BLOCK || Q == MOE_QUANT_W4A8) ? 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
-  static constexpr int S = NWV == 8 ? 2 : (Q == MOE_QUANT_W4A8 ? 4 : 3);  // stages in flight
+  static constexpr int S = Q == MOE_QUANT_W4A8 ? 4 : (NWV == 8 ? 2 : 3);  // stages in flight
   // loads per wave per stage: weight fragments, token fragments, scales
   static constexpr int LOADS = TILES * QT<Q>::AV / NWV + NT * 2 / NWV + (SC_BYTES ? 1 : 0);
   static_assert(S * STAGE <= 160 * 1024 - 4096, "stage buffers exceed the LDS");
@@ -305,12 +308,12 @@ __device__ __forceinline__ void lds_epilogue1(const GemmArgs& g, const f32x4 (&a
   }
 }
 
-template <int PHASE, int Q, int ACT, int WC, int NWV, bool PERSIST>
+template <int PHASE, int Q, int ACT, int WC, int NWV, bool PERSIST, int WT = 4>
 __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
   using T = QT<Q>;
-  using C = LdsCfg<Q, WC, NWV>;
+  using C = LdsCfg<Q, WC, NWV, WT>;
   // WT x NW: one wave's weight tiles x token tiles; BM: token rows of the workgroup
-  constexpr int WT = 4, NW = 8, NT = C::NT, BM = NT * 16, S = C::S, WR = C::WR;
+  constexpr int NW = 8, NT = C::NT, BM = NT * 16, S = C::S, WR = C::WR;
   constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
   // one array per stage: the compiler then sees that a stage's LDS reads do
   // not alias the LDS-DMA writes into the other stages and does not wait for them
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[S > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[S > 3 ? C::STAGE : 16];
-  __shared__ float lds_amax[PHASE == 1 && Q == MOE_QUANT_FP8_BLOCK ? 4 * BM : 1];
+  __shared__ float lds_amax[PHASE == 1 && Q == MOE_QUANT_FP8_BLOCK ? NWV * BM : 1];
   auto stage_buf = [&](auto bufc) -> uint8_t* {
     constexpr int B = decltype(bufc)::value;
     if constexpr (B == 0) return lds_s0;
@@ -373,12 +376,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       }
       bsrc[q] = uint32_t(brow) * uint32_t(g.K) + grp * 32;
     }
-    // scales of a stage: fp8-block weight scales (wave 0 and 3) and token-row
-    // scales (waves 1, 2); W4A8 group scales (every wave loads the same)
+    // scales of a stage: fp8-block token-row scales (waves 1, 2) and weight
+    // scales (every other wave, the same values); W4A8 group scales (every
+    // wave loads the same)
     const float* ssrc = nullptr;
     int sdst = 0;
     if (Q == MOE_QUANT_FP8_BLOCK) {
-      if (wave == 0 || wave == 3) {
+      if (wave != 1 && wave != 2) {
         const int t = min(wg_tile0 + (lane & 15), g.tiles - 1);
         const int rb = PHASE == 1 ? w13_row_block(t, g.I, GATED) : t / 8;
         ssrc = g.w_scale + (size_t(e) * (g.N / 128) + rb) * kblocks;
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
     if (S > 3 && st + 2 < nst) step(std::integral_constant<int, 2 % S>{}, st + 2);
     // drain the surplus loads before the LDS is handed back
     wait_vm_then_barrier<0>();
-    if constexpr (NWV == 8 && PHASE == 1) {
+    if constexpr (NWV == 8 && WC == 2 && PHASE == 1) {
       static_assert(Q == MOE_QUANT_FP8_TENSOR && C::STAGE >= 128 * (256 + 16), "8-wave GEMM1 tile");
       lds_epilogue1<ACT, WT, NW>(g, acc, e, row0, wr, wc, ct, (nvalid + 15) >> 4, wg_tile0,
                                  active, lds_s0, lds_s1);
@@ -578,6 +582,14 @@ hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
       const dim3 pgrid(c.kind == 3 ? std::min<unsigned>(grid.x, unsigned(persistent_slots()))
                                    : grid.x);
       if (c.nt == 8) {
+        // int4 and block-scaled weights: 8 waves of 2 weight tiles each, two
+        // waves per SIMD, so that one wave's conversions and scale FMAs run
+        // under the other's MFMAs
+        if constexpr (Q == MOE_QUANT_W4A8 || Q == MOE_QUANT_FP8_BLOCK) {
+          if (c.kind == 3) gemm_lds<PHASE, Q, ACT, 1, 8, true, 2><<<pgrid, dim3(512), 0, st>>>(a);
+          else gemm_lds<PHASE, Q, ACT, 1, 8, false, 2><<<pgrid, dim3(512), 0, st>>>(a);
+          return hipGetLastError();
+        }
         if (c.kind == 3) gemm_lds<PHASE, Q, ACT, 1, 4, true><<<pgrid, block, 0, st>>>(a);
         else gemm_lds<PHASE, Q, ACT, 1, 4, false><<<pgrid, block, 0, st>>>(a);
         return hipGetLastError();
