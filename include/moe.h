@@ -117,8 +117,9 @@ typedef struct moe_problem {
   int32_t quant;        /* enum moe_quant                                        */
   int32_t block_m;      /* alignment block (rows per GEMM tile): 0 = library
                            choice, else 16, 64, 128 or 256 (256: fp8
-                           per-tensor mode only).  Every call of one layer pass
-                           must see the same resolved value (moe_block_m).      */
+                           per-tensor and W4A8 modes only).  Every call of one
+                           layer pass must see the same resolved value
+                           (moe_block_m).                                        */
 } moe_problem;
 
 /* Packed weights (outputs of moe_pack_w13 / moe_pack_w2) and scales. */

@@ -232,14 +232,20 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
 // MFMAs).  8 waves of 4 tiles, WC = 2: 256 x 256, two stages; one wave's
 // LDS reads run under the other's MFMAs, and each weight byte serves twice
 // the tokens.
-template <int Q, int WC, int NWV, int WT = 4> struct LdsCfg {
+template <int Q, int WC, int NWV, int WT = 4, int NW = 8> struct LdsCfg {
   static constexpr int WR = NWV / WC;
-  static constexpr int TILES = WT * WR, NT = 8 * WC;  // weight / token tiles per workgroup
+  static constexpr int TILES = WT * WR, NT = NW * WC;  // weight / token tiles per workgroup
   static constexpr int A_BYTES = TILES * QT<Q>::FRAG;
   static constexpr int B_BYTES = NT * 2048;
   static constexpr int SC_BYTES = (Q == MOE_QUANT_FP8_BLOCK || Q == MOE_QUANT_W4A8) ? 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
-  static constexpr int S = Q == MOE_QUANT_W4A8 ? 4 : (NWV == 8 ? 2 : 3);  // stages in flight
+  // stages: as many as fit, at most 4
+#ifdef MOE_LDS_MAX_STAGES
+  static constexpr int SMAX = MOE_LDS_MAX_STAGES;
+#else
+  static constexpr int SMAX = 4;
+#endif
+  static constexpr int S = (160 * 1024 - 4096) / STAGE < SMAX ? (160 * 1024 - 4096) / STAGE : SMAX;
   // loads per wave per stage: weight fragments, token fragments, scales
   static constexpr int LOADS = TILES * QT<Q>::AV / NWV + NT * 2 / NWV + (SC_BYTES ? 1 : 0);
   static_assert(S * STAGE <= 160 * 1024 - 4096, "stage buffers exceed the LDS");
@@ -308,12 +314,13 @@ __device__ __forceinline__ void lds_epilogue1(const GemmArgs& g, const f32x4 (&a
   }
 }
 
-template <int PHASE, int Q, int ACT, int WC, int NWV, bool PERSIST, int WT = 4>
+template <int PHASE, int Q, int ACT, int WC, int NWV, bool PERSIST, int WT = 4, int NW = 8>
 __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
   using T = QT<Q>;
-  using C = LdsCfg<Q, WC, NWV, WT>;
+  using C = LdsCfg<Q, WC, NWV, WT, NW>;
   // WT x NW: one wave's weight tiles x token tiles; BM: token rows of the workgroup
-  constexpr int NW = 8, NT = C::NT, BM = NT * 16, S = C::S, WR = C::WR;
+  constexpr int NT = C::NT, BM = NT * 16, S = C::S, WR = C::WR;
+  static_assert(S >= 2, "two stages at least");
   constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
   // one array per stage: the compiler then sees that a stage's LDS reads do
   // not alias the LDS-DMA writes into the other stages and does not wait for them
@@ -485,6 +492,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
             }
           }
         }
+        // 16 token tiles: keep each tile's LDS reads next to its MFMAs (read
+        // all ahead, their 128 registers and the accumulators do not fit)
+        if constexpr (NW > 8) __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -594,9 +604,18 @@ hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
         else gemm_lds<PHASE, Q, ACT, 1, 4, false><<<pgrid, block, 0, st>>>(a);
         return hipGetLastError();
       }
+      if constexpr (Q == MOE_QUANT_W4A8) {
+        // 8 waves of 2 weight tiles x 16 token tiles: 256 x 256, each
+        // converted weight fragment feeds 16 MFMAs
+        if (c.nt == 16) {
+          if (c.kind == 3) gemm_lds<PHASE, Q, ACT, 1, 8, true, 2, 16><<<pgrid, dim3(512), 0, st>>>(a);
+          else gemm_lds<PHASE, Q, ACT, 1, 8, false, 2, 16><<<grid, dim3(512), 0, st>>>(a);
+          return hipGetLastError();
+        }
+      }
       if constexpr (Q == MOE_QUANT_FP8_TENSOR) {
-        // 8 waves, 256 x 256: one workgroup per tile (the int4 unpacking and
-        // the persistent loop's state do not fit the registers of 8 waves)
+        // 8 waves, 256 x 256: one workgroup per tile (the persistent loop's
+        // state does not fit the registers of 8 waves of 4 x 8 tiles)
         if (c.nt == 16 && c.kind == 2) {
           gemm_lds<PHASE, Q, ACT, 2, 8, false><<<grid, dim3(512), 0, st>>>(a);
           return hipGetLastError();

@@ -139,11 +139,12 @@ int make_plan(const moe_problem* p, Plan* plan) {
   // ---- tile table: the alignment block follows the expected rows per
   // expert.  Decode-sized problems stream weights 16 token rows at a time;
   // with many rows per expert the tiled kernels stage 128 token rows in LDS
-  // and reuse every weight fragment across them; fp8 per-tensor weights with
-  // 256 or more rows per expert take 256 token rows per block, so that each
-  // weight byte brought into the LDS serves twice the tokens.
+  // and reuse every weight fragment across them; fp8 per-tensor and int4
+  // weights with 256 or more rows per expert take 256 token rows per block,
+  // so that each weight byte brought into the LDS (and each int4 fragment
+  // converted to e4m3) serves twice the tokens.
   const int64_t rows_per_expert = q.A / std::max(1, p->E);
-  const bool wide_ok = p->quant == MOE_QUANT_FP8_TENSOR;
+  const bool wide_ok = p->quant == MOE_QUANT_FP8_TENSOR || p->quant == MOE_QUANT_W4A8;
   if (p->block_m != 0) {
     q.BM = p->block_m;
   } else if (rows_per_expert >= MOE_WIDE_MIN_ROWS && wide_ok) {
@@ -154,7 +155,8 @@ int make_plan(const moe_problem* p, Plan* plan) {
     q.BM = 16;
   }
   if (q.BM == 256 && !wide_ok)
-    return fail(MOE_ERR_UNSUPPORTED, "block_m = 256 runs for the fp8 per-tensor mode only");
+    return fail(MOE_ERR_UNSUPPORTED,
+                "block_m = 256 runs for the fp8 per-tensor and int4 (W4A8) modes only");
   const int64_t nz = std::min<int64_t>(p->E, q.A);
   q.max_blocks = std::min<int64_t>(q.A, (q.A + nz * (q.BM - 1)) / q.BM);
   q.max_rows = q.max_blocks * q.BM;
@@ -175,10 +177,14 @@ int make_plan(const moe_problem* p, Plan* plan) {
     // fp8 / int4 weights at 128-row blocks: weights and tokens staged in LDS by
     // direct-to-LDS loads, several k-steps in flight, one persistent
     // workgroup per CU taking the tiles in rounds (MOE_LDS_KIND 2 at build
-    // time: one workgroup per tile).  256-row blocks: 8 waves, one workgroup
-    // per tile.
+    // time: one workgroup per tile).  256-row blocks: 8 waves; fp8 one
+    // workgroup per tile, int4 persistent.
     const bool lds = q.BM >= 128 && p->quant != MOE_QUANT_BF16;
-    q.g1 = GemmCfg{lds ? (q.BM == 256 ? 2 : MOE_LDS_KIND) : 1, q.BM / 16, 4, 1, 4};
+#ifndef MOE_WIDE_KIND_W4A8
+#define MOE_WIDE_KIND_W4A8 3
+#endif
+    const int wide_kind = p->quant == MOE_QUANT_W4A8 ? MOE_WIDE_KIND_W4A8 : 2;
+    q.g1 = GemmCfg{lds ? (q.BM == 256 ? wide_kind : MOE_LDS_KIND) : 1, q.BM / 16, 4, 1, 4};
     q.g2 = q.g1;
   }
 

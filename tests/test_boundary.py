@@ -65,7 +65,7 @@ def test_valid_problems(plan):
     (dict(act=7), moe.MOE_ERR_INVALID_ARG),
     (dict(quant=9), moe.MOE_ERR_INVALID_ARG),
     (dict(block_m=17), moe.MOE_ERR_INVALID_ARG),
-    (dict(block_m=256), moe.MOE_ERR_UNSUPPORTED),                 # 256: fp8 per-tensor only
+    (dict(block_m=256), moe.MOE_ERR_UNSUPPORTED),                 # 256: fp8 per-tensor, W4A8
     (dict(H=200), moe.MOE_ERR_ALIGNMENT),
     (dict(I=500), moe.MOE_ERR_ALIGNMENT),                       # gated bf16 needs 32
     (dict(I=96, act="relu2"), moe.MOE_ERR_ALIGNMENT),           # non-gated needs 128

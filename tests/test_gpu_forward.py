@@ -181,7 +181,7 @@ def test_invalid_call_enqueues_nothing():
 
 TILED = [(q, a, bm) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
          for a in ("silu", "relu2") for bm in (64, 128)] + \
-        [("fp8_tensor", a, 256) for a in ("silu", "relu2")]
+        [(q, a, 256) for q in ("fp8_tensor", "w4a8") for a in ("silu", "relu2")]
 
 
 @pytest.mark.parametrize("quant,act,bm", TILED)
@@ -203,13 +203,14 @@ def test_forward_tiled_ragged(quant, act, bm):
     assert_close(out.float().cpu().numpy(), ref, quant, f"tiled {quant} {act} bm={bm}")
 
 
-@pytest.mark.parametrize("act", ["silu", "relu2"])
-def test_forward_wide_blocks_by_default(act):
-    """fp8 per-tensor with 256+ rows per expert takes 256-row blocks by
-    itself: several full blocks per expert, ragged last blocks, and blocks
-    whose second half of token tiles is empty or partly filled."""
-    cfg = ad_hoc(94, "fp8_tensor", act, H=512, I=384, E_routed=4, top_k=2, n_shared=1)
-    say(f"wide fp8_tensor {act}")
+@pytest.mark.parametrize("quant,act", [("fp8_tensor", "silu"), ("fp8_tensor", "relu2"),
+                                       ("w4a8", "silu"), ("w4a8", "relu2")])
+def test_forward_wide_blocks_by_default(quant, act):
+    """fp8 per-tensor and int4 with 256+ rows per expert take 256-row blocks
+    by themselves: several full blocks per expert, ragged last blocks, and
+    blocks whose second half of token tiles is empty or partly filled."""
+    cfg = ad_hoc(94, quant, act, H=512, I=384, E_routed=4, top_k=2, n_shared=1)
+    say(f"wide {quant} {act}")
     W = synth.make_weights(cfg, seed=779)
     T = 700
     tok = synth.make_tokens(cfg, T, seed=80)
@@ -219,4 +220,4 @@ def test_forward_wide_blocks_by_default(act):
     out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
     torch.cuda.synchronize()
     ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"], sc["a1"], sc["a2"])
-    assert_close(out.float().cpu().numpy(), ref, "fp8_tensor", f"wide {act}")
+    assert_close(out.float().cpu().numpy(), ref, quant, f"wide {quant} {act}")
