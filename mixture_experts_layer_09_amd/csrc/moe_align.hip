@@ -28,6 +28,13 @@ namespace {
 constexpr int kThreads = kAlignChunk;  // 1024 threads, 16 waves
 constexpr int kWaves = kThreads / 64;
 
+// The decode prologue quantises x itself for up to this many passes of one
+// 8-element group per thread (beyond, a grid-wide quantisation launch).
+#ifndef MOE_FUSE_QUANT_MAX_PASSES
+#define MOE_FUSE_QUANT_MAX_PASSES 4
+#endif
+constexpr int kFuseQuantMaxPasses = MOE_FUSE_QUANT_MAX_PASSES;
+
 // Rank of this lane among the active lanes with the same expert below it, and
 // the number of active lanes with that expert.  The lanes sharing this lane's
 // expert are found with one ballot per bit of the expert id: a lane matches
@@ -199,6 +206,15 @@ __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
   int* sids = smem;
   const int Kp = a.top_k + a.n_shared;
   const int wave = threadIdx.x >> 6;
+  // x for the quantisation is loaded first, so that its memory latency
+  // overlaps the routing's
+  const int n8 = QM != 0 ? a.T * a.H / 8 : 0;
+  u32x4 xv[QM != 0 ? kFuseQuantMaxPasses : 1];
+#pragma unroll
+  for (int q = 0; q < (QM != 0 ? kFuseQuantMaxPasses : 0); ++q) {
+    const int i = q * kThreads + threadIdx.x;
+    xv[q] = i < n8 ? ld16(a.x + size_t(i) * 8) : u32x4{0, 0, 0, 0};
+  }
   if (a.logits) {
     constexpr int TPW = 64 / L;
     for (int base = 0; base < a.T; base += kWaves * TPW) {
@@ -217,12 +233,12 @@ __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
   }
   if (QM != 0) {
     // 8 elements per thread and pass; a DPP row of 16 lanes is one 128-column group
-    const int n8 = a.T * a.H / 8;
     const float s1 = QM == 1 ? *a.a1 : 1.f;
-    for (int base = 0; base < n8; base += kThreads) {
-      const int i = base + threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < kFuseQuantMaxPasses; ++q) {
+      const int i = q * kThreads + threadIdx.x;
       const bool in = i < n8;
-      const u32x4 v = in ? ld16(a.x + size_t(i) * 8) : u32x4{0, 0, 0, 0};
+      const u32x4 v = xv[q];
       float f[8];
       float amax = 0.f;
 #pragma unroll
@@ -384,10 +400,6 @@ hipError_t prologue_q(const moe_problem& p, const PrologueArgs& a, size_t sm,
 }
 }  // namespace
 
-#ifndef MOE_FUSE_QUANT_MAX_PASSES
-#define MOE_FUSE_QUANT_MAX_PASSES 4
-#endif
-constexpr int kFuseQuantMaxPasses = MOE_FUSE_QUANT_MAX_PASSES;
 
 bool prologue_fits(const moe_problem& p, const Plan& q) {
   return q.chunks <= 1 && p.T <= 128 && p.E_routed <= kMaxRouted;

@@ -32,6 +32,46 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t k) {
   return (uint64_t(hi) << 32) | lo;
 }
 
+// Maximum of a 32-bit value over the lane group; every lane of the group gets
+// it.  Lanes a DPP step does not reach read 0 (bound_ctrl), the identity of an
+// unsigned maximum, so each step folds into one v_max_u32 with a DPP operand.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xF, true));
+  return v > o ? v : o;
+}
+template <int L>
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+  v = dpp_umax<kDppXor1, 0xF>(v);
+  v = dpp_umax<kDppXor2, 0xF>(v);
+  v = dpp_umax<kDppHalfMirror, 0xF>(v);
+  v = dpp_umax<kDppMirror, 0xF>(v);
+  if (L == 16) return v;
+  v = dpp_umax<kDppBcast15, 0xA>(v);
+  v = dpp_umax<kDppBcast31, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Sorts a lane's keys in descending order (bitonic network, N a power of 2).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&k)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size *= 2)
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride /= 2)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;  // this half of the sequence descending
+          const uint64_t a = k[i], b = k[j];
+          const bool swap = desc ? (a < b) : (a > b);
+          k[i] = swap ? b : a;
+          k[j] = swap ? a : b;
+        }
+      }
+}
+
 // Sum over the lane group; every lane of the group gets it.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
@@ -63,19 +103,26 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, bool 
     v[i] = in ? row[j] : 0.f;
     key[i] = in ? (uint64_t(float_order_bits(v[i])) << 32) | uint32_t(~uint32_t(j)) : 0;
   }
+  // Each lane sorts its keys (value's order bits, then the complemented
+  // index: larger value first, lower index first on ties); round r takes the
+  // largest head over the group -- the value's maximum, then among the lanes
+  // holding that value the lowest index -- and the lane holding it drops its
+  // head.  The picks come out in the order of the full keys.
+  sort_desc<NPL>(key);
   float my_val = 0.f;  // lane r of the group keeps the r-th selected logit
   int my_idx = 0;
   float vmax = 0.f;
   for (int r = 0; r < top_k; ++r) {
-    uint64_t best = key[0];
+    const uint32_t hv = uint32_t(key[0] >> 32), hj = ~uint32_t(key[0]);
+    const uint32_t gv = group_umax<L>(hv);
+    const uint32_t gj = ~group_umax<L>(hv == gv ? ~hj : 0u);  // lowest index at that value
+    const int j = int(gj);
+    const float val = float_from_order_bits(gv);
+    if (hv == gv && hj == gj) {  // this lane held the pick: drop it
 #pragma unroll
-    for (int i = 1; i < NPL; ++i) best = key[i] > best ? key[i] : best;
-    const uint64_t w = group_max_u64<L>(best);
-    const int j = int(~uint32_t(w));
-    const float val = float_from_order_bits(uint32_t(w >> 32));
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (j == gl + L * i) key[i] = 0;
+      for (int i = 0; i + 1 < NPL; ++i) key[i] = key[i + 1];
+      key[NPL - 1] = 0;
+    }
     if (r == 0) vmax = val;  // the first pick is the largest logit
     if (gl == r) {
       my_val = val;
