@@ -16,7 +16,8 @@
 //   A <= 1024 : one workgroup, one launch -- and, for decode-sized batches,
 //               together with the routing and the fp8 quantisation of x in the
 //               same kernel;
-//   A >  1024 : histogram -> scan -> scatter, three launches.
+//   A <= 4096 : one workgroup ranking the chunks one after another;
+//   A >  4096 : histogram -> scan -> scatter, three launches.
 #include "moe_device.hpp"
 #include "moe_launch.hpp"
 #include "moe_route.hpp"
@@ -271,6 +272,65 @@ __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
                  a.offsets, a.npad);
 }
 
+// One workgroup for 1024 < A <= kMidChunks * 1024: the chunks of 1024
+// assignments are ranked one after another -- per expert, the count of the
+// earlier chunks, plus the earlier waves of this chunk, plus the lane's rank
+// in its wave -- then the padded offsets and the scatter.  Shared memory:
+// run[E], wcnt[kWaves][E], off[E+1], tmp.
+constexpr int kMidChunks = 4;
+__global__ __launch_bounds__(kThreads) void align_mid(const int32_t* __restrict__ ids, int A,
+                                                      int E, int BM,
+                                                      int32_t* __restrict__ sorted_ids,
+                                                      int32_t* __restrict__ block_expert,
+                                                      int32_t* __restrict__ g_offsets,
+                                                      int32_t* __restrict__ g_npad) {
+  extern __shared__ int smem[];
+  int* run = smem;
+  int* wcnt = run + E;
+  int* off = wcnt + kWaves * E;
+  int* tmp = off + E + 1;
+  const int wave = threadIdx.x >> 6;
+  int ev[kMidChunks];
+#pragma unroll
+  for (int c = 0; c < kMidChunks; ++c) {
+    const int f = c * kThreads + threadIdx.x;
+    ev[c] = f < A ? ids[f] : -1;
+  }
+  for (int i = threadIdx.x; i < E; i += kThreads) run[i] = 0;
+  const int nbits = id_bits(E);
+  int rank[kMidChunks];
+#pragma unroll
+  for (int c = 0; c < kMidChunks; ++c) {
+    for (int i = threadIdx.x; i < kWaves * E; i += kThreads) wcnt[i] = 0;
+    __syncthreads();
+    const int e = ev[c];
+    const bool valid = c * kThreads + int(threadIdx.x) < A && e >= 0 && e < E;
+    int r, cnt;
+    match_rank(e, valid, nbits, r, cnt);
+    if (valid && r == 0) wcnt[wave * E + e] = cnt;
+    __syncthreads();
+    // per expert: the waves' bases in place, the running count advanced
+    for (int x = threadIdx.x; x < E; x += kThreads) {
+      int acc = run[x];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int v = wcnt[w * E + x];
+        wcnt[w * E + x] = acc;
+        acc += v;
+      }
+      run[x] = acc;
+    }
+    __syncthreads();
+    rank[c] = valid ? wcnt[wave * E + e] + r : -1;
+    __syncthreads();  // wcnt is cleared for the next chunk
+  }
+  padded_offsets(run, off, E, BM, tmp, g_offsets, g_npad);
+#pragma unroll
+  for (int c = 0; c < kMidChunks; ++c)
+    if (rank[c] >= 0) sorted_ids[off[ev[c]] + rank[c]] = c * kThreads + threadIdx.x;
+  fill_tail(run, off, E, BM, A, sorted_ids, block_expert);
+}
+
 // Chunk histogram: hist[c][e] = assignments of chunk c with expert e.
 __global__ __launch_bounds__(kThreads) void align_count(const int32_t* __restrict__ ids, int A,
                                                         int E, int32_t* __restrict__ hist) {
@@ -361,6 +421,14 @@ hipError_t launch_align(const moe_problem& p, const Plan& q, const int32_t* ids,
     if (err != hipSuccess) return err;
     align_small<<<1, kThreads, sm, stream>>>(ids, A, E, BM, sorted_ids, block_expert, offsets,
                                              num_padded);
+    return hipGetLastError();
+  }
+  if (q.chunks <= kMidChunks) {
+    const size_t sm = (size_t(E) + size_t(kWaves) * E + (E + 1) + kWaves + 1) * 4;
+    hipError_t err = allow_lds(align_mid, sm);
+    if (err != hipSuccess) return err;
+    align_mid<<<1, kThreads, sm, stream>>>(ids, A, E, BM, sorted_ids, block_expert, offsets,
+                                           num_padded);
     return hipGetLastError();
   }
   align_count<<<q.chunks, kThreads, size_t(E) * 4, stream>>>(ids, A, E, scratch);

@@ -138,6 +138,9 @@ RA_CASES = [  # T, E_routed, top_k, n_shared, renormalize, block_m
     (64, 8, 2, 0, False, 0), (128, 128, 6, 0, True, 0), (93, 1000, 11, 0, True, 0),
     (256, 512, 10, 1, True, 0), (4096, 512, 10, 1, True, 0), (8192, 20, 8, 0, True, 0),
     (2, 1020, 60, 4, True, 0),
+    # 1024 < A <= 4096 (one workgroup, chunk after chunk) and just past it
+    (100, 1000, 30, 2, True, 0), (200, 16, 16, 4, False, 0), (128, 128, 32, 0, True, 0),
+    (129, 128, 32, 0, True, 0),
     # small batches: both routing layouts, 64 slots per token, explicit blocks
     (8, 128, 8, 0, True, 0), (3, 1000, 11, 2, False, 0), (1, 1020, 60, 4, True, 0),
     (5, 8, 2, 0, True, 16), (21, 40, 3, 0, False, 64)]
