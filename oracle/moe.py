@@ -10,10 +10,11 @@ Steps, in the order the pages chain them:
             the GEMM M tile (Qwen3-Next FP8 page, BLOCK_SIZE_M in the Triton
             config; W4A8 page, ``expert_offsets``/``problem_sizes``).
   quant  -- fp8 activation quantisation for the fp8 / W4A8 modes.
-  GEMM1  -- h = W13[e] . x_t, then the activation: SiLU(gate) * up for gated
-            layers, relu(h)^2 for the non-gated one (SwiGLU-fusion page,
-            epilogue; TRTLLM-Gen page, non-gated relu2); the intermediate is
-            stored at half width in the compute format.
+  GEMM1  -- h = W13[e] . x_t, then the activation: SiLU(gate) * up or
+            GELU_tanh(gate) * up for gated layers, relu(h)^2 for the non-gated
+            one (SwiGLU-fusion page, epilogue; Blackwell gated-MoE page,
+            gated activation list; TRTLLM-Gen page, non-gated relu2); the
+            intermediate is stored at half width in the compute format.
   GEMM2  -- y = W2[e] . a, weighted by the routing weight and summed back into
             the token's row (Blackwell gated-MoE page: FC2 is non-gated and
             routing/scatter are unchanged).
@@ -321,6 +322,17 @@ def _silu(g):
     return g / (1.0 + np.exp(-g))
 
 
+# Gated activations: the gate half goes through one of these, times the up half
+# (flashinfer PR 4329 page, sections 1 and 3: silu and gelu_tanh as gated
+# activations).  gelu_tanh is GELU in its tanh approximation,
+# 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))).
+def _gelu_tanh(g):
+    return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+
+
+GATE_FN = {"silu": _silu, "gelu_tanh": _gelu_tanh}
+
+
 def _activate(h, act, I, layout_g):
     if act == "relu2":
         r = np.maximum(h, 0.0)
@@ -332,7 +344,7 @@ def _activate(h, act, I, layout_g):
         p = h.reshape(h.shape[0], I // layout_g, 2, layout_g)
         gate = p[:, :, 0, :].reshape(h.shape[0], I)
         up = p[:, :, 1, :].reshape(h.shape[0], I)
-    return _silu(gate) * up
+    return GATE_FN[act](gate) * up
 
 
 # --------------------------------------------------------------------------
@@ -357,7 +369,7 @@ def moe_forward(x, w13, w2, *, quant, act, E_routed, top_k, renormalize,
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
     E = E_routed + n_shared
-    gated = act == "silu"
+    gated = act in GATE_FN
     if logits is not None:
         ids, wts = route(logits, top_k, renormalize, n_shared, shared_gate)
     else:

@@ -24,7 +24,7 @@ class MoEConfig:
     top_k: int        # routed slots per token
     n_shared: int     # shared-expert slots appended after the routed ones
     shared_gate: float
-    act: str          # "silu" (gated SiLU*up) or "relu2" (non-gated relu(x)^2)
+    act: str          # "silu" / "gelu_tanh" (gated: act(gate)*up) or "relu2" (relu(x)^2)
     quant: str        # "bf16" | "fp8_tensor" | "fp8_block" | "w4a8"
     renormalize: bool
     Ms: Tuple[int, ...]
@@ -40,7 +40,7 @@ class MoEConfig:
 
     @property
     def gated(self) -> bool:
-        return self.act == "silu"
+        return self.act != "relu2"
 
     @property
     def N1(self) -> int:

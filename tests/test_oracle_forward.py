@@ -41,6 +41,8 @@ def _torch_mlp(x, w13, w2, act, mid=None):
     I = w2.shape[1]
     if act == "silu":
         a = F.silu(x @ w13[:I].T) * (x @ w13[I:].T)
+    elif act == "gelu_tanh":
+        a = F.gelu(x @ w13[:I].T, approximate="tanh") * (x @ w13[I:].T)
     else:
         a = F.relu(x @ w13.T) ** 2
     if mid is not None:
@@ -54,10 +56,10 @@ def _fwd(x, w13, w2, **kw):
     return oracle.moe_forward(x, w13, w2, **base)["out"]
 
 
-@pytest.mark.parametrize("act", ["silu", "relu2"])
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh", "relu2"])
 def test_single_expert_is_plain_mlp(act):
     H, I, T = 64, 48, 9
-    N1 = 2 * I if act == "silu" else I
+    N1 = I if act == "relu2" else 2 * I
     w13, w2, x = _mk_bf16(1, N1, H, I, T, 1)
     lg = np.zeros((T, 1), np.float32)
     got = _fwd(x, w13, w2, act=act, E_routed=1, top_k=1, logits=lg, storage="exact")
@@ -89,14 +91,33 @@ def test_token_permutation_equivariant():
     np.testing.assert_allclose(a[perm], b, rtol=1e-13, atol=1e-14)
 
 
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
 @pytest.mark.parametrize("G", [1, 4, 16, 32])
-def test_interleaved_equals_split_bf16(G):
+def test_interleaved_equals_split_bf16(G, act):
     E, H, I, T = 3, 32, 32, 10
     w13, w2, x = _mk_bf16(E, 2 * I, H, I, T, 6)
     lg = R(7).standard_normal((T, E)).astype(np.float32)
-    a = _fwd(x, w13, w2, E_routed=E, top_k=2, logits=lg)
-    b = _fwd(x, oracle.interleave_rows(w13, G), w2, E_routed=E, top_k=2, logits=lg, layout_g=G)
+    a = _fwd(x, w13, w2, act=act, E_routed=E, top_k=2, logits=lg)
+    b = _fwd(x, oracle.interleave_rows(w13, G), w2, act=act, E_routed=E, top_k=2, logits=lg,
+             layout_g=G)
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_gelu_tanh_gate_closed_forms():
+    """The gelu_tanh gate, from its definition rather than a library: g(0) = 0,
+    g(v) - g(-v) = v (the tanh term is odd), g(v) -> v and g(-v) -> 0 for
+    large v, and at v = 1 the value 0.5 (1 + tanh(1.044715 sqrt(2/pi)))."""
+    from oracle.moe import GATE_FN
+    g = GATE_FN["gelu_tanh"]
+    v = np.linspace(-6, 6, 241)
+    assert g(np.array(0.0)) == 0.0
+    np.testing.assert_allclose(g(v) - g(-v), v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(g(np.array([30.0, -30.0])), [30.0, 0.0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g(np.array(1.0)), 0.8411919906082768, rtol=1e-15)
+    # within 1e-3 of the erf form it approximates, and not equal to SiLU
+    erf_gelu = 0.5 * v * (1 + np.vectorize(__import__("math").erf)(v / np.sqrt(2)))
+    assert np.max(np.abs(g(v) - erf_gelu)) < 1e-3
+    assert np.max(np.abs(g(v) - GATE_FN["silu"](v))) > 0.1
 
 
 def test_interleave_layout_literal():
@@ -118,13 +139,14 @@ def test_half_swap():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("act", ["silu", "relu2"])
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh", "relu2"])
 def test_zero_padding_leaves_output_unchanged(act):
     E, H, I, T = 3, 32, 40, 8
-    N1 = 2 * I if act == "silu" else I
+    gated = act != "relu2"
+    N1 = 2 * I if gated else I
     w13, w2, x = _mk_bf16(E, N1, H, I, T, 10)
-    p13, p2, Ip = oracle.pad_intermediate(w13, w2, act == "silu")
-    assert Ip == (48 if act == "silu" else 128)
+    p13, p2, Ip = oracle.pad_intermediate(w13, w2, gated)
+    assert Ip == (48 if gated else 128)
     lg = R(11).standard_normal((T, E)).astype(np.float32)
     a = _fwd(x, w13, w2, act=act, E_routed=E, top_k=2, logits=lg)
     b = _fwd(x, p13, p2, act=act, E_routed=E, top_k=2, logits=lg)
@@ -228,7 +250,7 @@ def test_per_tensor_scale_algebra():
 def _fp8_tensor_case(act, seed):
     rng = R(seed)
     H, I, T = 256, 128, 12
-    N1 = 2 * I if act == "silu" else I
+    N1 = I if act == "relu2" else 2 * I
     w13f = rng.standard_normal((1, N1, H)) / 16
     w2f = rng.standard_normal((1, H, I)) / np.sqrt(I)
     s13 = np.array([np.abs(w13f).max() / 448], np.float32)
@@ -240,7 +262,7 @@ def _fp8_tensor_case(act, seed):
     return x, c13, s13, c2, s2, a1
 
 
-@pytest.mark.parametrize("act", ["silu", "relu2"])
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh", "relu2"])
 def test_fp8_tensor_single_expert_with_torch_casts(act):
     x, c13, s13, c2, s2, a1 = _fp8_tensor_case(act, 19)
     a2 = np.float32(4.0 / 448)
