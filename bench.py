@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the fused MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload cfg2_M64] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload cfg2_M64] [--act A] [--gpus 1]
 
 One step is one whole pass of the layer -- route + (fp8 quantise) + align,
 GEMM1 + activation, GEMM2 + combine -- over one batch of synthetic tokens
@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="cfg2_M64")
+    ap.add_argument("--act", choices=("silu", "relu2", "gelu_tanh"), default=None,
+                    help="replace the workload's activation (same shapes otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -229,6 +231,11 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     cfg, M = workload(args.workload)
+    key = args.workload
+    if args.act is not None and args.act != cfg.act:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, act=args.act)
+        key = f"{args.workload}_{args.act}"
     W = synth.make_weights(cfg)
     tok = synth.make_tokens(cfg, M)
     sc = synth.make_act_scales(cfg, tok["x_bits"])
@@ -276,7 +283,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gemm1_act", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_record(args.workload),
+                     "traffic": traffic_record(key),
                      "algorithmic_bytes_per_launch": int(alg["gemm1_bytes"]),
                      "avg_launch_us": round(float(g1), 2)},
         "layer": {"gpu_ms_per_step": round(gpu_ms, 4), "us_route_align_quant": round(float(pre), 2),

@@ -79,10 +79,14 @@ enum moe_status {
   MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed           */
 };
 
-/* Activation of GEMM1 ([TRTLLM] section 1 ActivationType; [GATED] section 1). */
+/* Activation of GEMM1 ([TRTLLM] section 1 ActivationType; [GATED] sections 1
+   and 3: silu and gelu_tanh among the gated activations). */
 enum moe_act {
-  MOE_ACT_SILU_GATED = 0, /* a = SiLU(gate) * up, W13 holds 2I rows          */
-  MOE_ACT_RELU2 = 1       /* a = relu(h)^2, non-gated, W13 holds I rows      */
+  MOE_ACT_SILU_GATED = 0,      /* a = SiLU(gate) * up, W13 holds 2I rows     */
+  MOE_ACT_RELU2 = 1,           /* a = relu(h)^2, non-gated, W13 holds I rows */
+  MOE_ACT_GELU_TANH_GATED = 2  /* a = GELU_tanh(gate) * up, 2I rows, where
+                                  GELU_tanh(g) = 0.5 g (1 + tanh(sqrt(2/pi)
+                                  (g + 0.044715 g^3)))                       */
 };
 
 /* Weight / activation formats. */

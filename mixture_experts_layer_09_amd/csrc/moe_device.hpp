@@ -102,6 +102,16 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
 }
 
+// GELU, tanh form: 0.5 g (1 + tanh(u)), u = sqrt(2/pi) (g + 0.044715 g^3).
+// Since 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), this is g / (1 + 2^z) with
+// z = -2 log2(e) u = g (c1 + c3 g^2): one exp2, one reciprocal, as SiLU.
+__device__ __forceinline__ float gelu_tanh(float g) {
+  constexpr float c1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  constexpr float c3 = c1 * 0.044715f;
+  const float z = g * __builtin_fmaf(c3, g * g, c1);
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
+}
+
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
   constexpr int RG = 4 / KS;       // waves along the weight rows
   constexpr int TPW = RG * WT;     // row tiles per workgroup
   constexpr int D = Q == MOE_QUANT_BF16 ? 4 : 2;  // k-steps loaded ahead
-  constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
+  constexpr bool GATED = PHASE == 1 && act_gated(ACT);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rg = wave % RG, kp = wave / RG;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
       for (int i = 0; i < 4; ++i) {
         if (GATED) {
           const float gt = alpha * acc[2 * v][i], up = alpha * acc[2 * v + 1][i];
-          a[v][i] = silu(gt) * up;
+          a[v][i] = gate_act<ACT>(gt) * up;
         } else {
           const float h = fmaxf(alpha * acc[v][i], 0.f);
           a[v][i] = h * h;
@@ -365,6 +365,8 @@ hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, cons
     return launch_gemm_tiled(1, p, q.g1, a, stream);
   }
   const dim3 grid = stream_grid(q.g1, a.tiles, q.max_blocks);
+  if (p.act == MOE_ACT_GELU_TANH_GATED)
+    return dispatch_quant<1, MOE_ACT_GELU_TANH_GATED>(p.quant, q.g1, grid, a, stream);
   if (q.gated) return dispatch_quant<1, MOE_ACT_SILU_GATED>(p.quant, q.g1, grid, a, stream);
   return dispatch_quant<1, MOE_ACT_RELU2>(p.quant, q.g1, grid, a, stream);
 }

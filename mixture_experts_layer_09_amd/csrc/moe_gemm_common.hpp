@@ -47,6 +47,16 @@ __device__ __forceinline__ i32x8 fp8_pair(const u32x4& lo, const u32x4& hi) {
   return r;
 }
 
+// Gated activations pair a gate and an up channel; relu2 is the one that is not.
+constexpr bool act_gated(int act) { return act != MOE_ACT_RELU2; }
+
+// The gate half's nonlinearity of a gated activation.
+template <int ACT>
+__device__ __forceinline__ float gate_act(float g) {
+  if constexpr (ACT == MOE_ACT_GELU_TANH_GATED) return gelu_tanh(g);
+  else return silu(g);
+}
+
 // Weight row block (128 rows, checkpoint order) of a packed W13 row tile.
 __device__ __forceinline__ int w13_row_block(int tile, int I, bool gated) {
   if (!gated) return tile / 8;

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
   constexpr int LROW = ROWB + 16;           // LDS row stride
   constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
   constexpr int PIECES = BM * CPR / 256;    // chunks per thread per stage
-  constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
+  constexpr bool GATED = PHASE == 1 && act_gated(ACT);
   constexpr int TPW = 4 * WT;               // row tiles per workgroup
   static_assert(PIECES >= 1 && BM * CPR % 256 == 0, "stage does not split over the threads");
 
@@ -266,7 +266,7 @@ __device__ __forceinline__ void lds_epilogue1(const GemmArgs& g, const f32x4 (&a
                                               int e, int row0, int wr, int wc, int ct,
                                               int ct_all, int wg_tile0, bool active,
                                               uint8_t* s0, uint8_t* s1) {
-  constexpr bool GATED = ACT == MOE_ACT_SILU_GATED;
+  constexpr bool GATED = act_gated(ACT);
   constexpr int NV = GATED ? WT / 2 : WT;  // 4-channel vectors per lane and token tile
   constexpr int OC = GATED ? 128 : 256;    // output channels (bytes) of the workgroup tile
   constexpr int OCP = OC + 16;
@@ -285,7 +285,7 @@ __device__ __forceinline__ void lds_epilogue1(const GemmArgs& g, const f32x4 (&a
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (GATED) {
-              a[i] = silu(alpha * acc[2 * v][c][i]) * (alpha * acc[2 * v + 1][c][i]);
+              a[i] = gate_act<ACT>(alpha * acc[2 * v][c][i]) * (alpha * acc[2 * v + 1][c][i]);
             } else {
               const float h = fmaxf(alpha * acc[v][c][i], 0.f);
               a[i] = h * h;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
   // WT x NW: one wave's weight tiles x token tiles; BM: token rows of the workgroup
   constexpr int NT = C::NT, BM = NT * 16, S = C::S, WR = C::WR;
   static_assert(S >= 2, "two stages at least");
-  constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
+  constexpr bool GATED = PHASE == 1 && act_gated(ACT);
   // one array per stage: the compiler then sees that a stage's LDS reads do
   // not alias the LDS-DMA writes into the other stages and does not wait for them
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[C::STAGE];
@@ -634,7 +634,6 @@ hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm_tiled(int phase, const moe_problem& p, const GemmCfg& c,
                              const GemmArgs& a, hipStream_t st) {
-  const bool gated = p.act == MOE_ACT_SILU_GATED;
 #define MOE_TQ(PH, ACT)                                                                      \
   switch (p.quant) {                                                                         \
     case MOE_QUANT_BF16: return dispatch_tiled<PH, MOE_QUANT_BF16, ACT>(c, a, st);           \
@@ -643,10 +642,10 @@ hipError_t launch_gemm_tiled(int phase, const moe_problem& p, const GemmCfg& c,
     case MOE_QUANT_W4A8: return dispatch_tiled<PH, MOE_QUANT_W4A8, ACT>(c, a, st);           \
   }
   if (phase == 1) {
-    if (gated) {
-      MOE_TQ(1, MOE_ACT_SILU_GATED)
-    } else {
-      MOE_TQ(1, MOE_ACT_RELU2)
+    switch (p.act) {
+      case MOE_ACT_SILU_GATED: MOE_TQ(1, MOE_ACT_SILU_GATED) break;
+      case MOE_ACT_GELU_TANH_GATED: MOE_TQ(1, MOE_ACT_GELU_TANH_GATED) break;
+      default: MOE_TQ(1, MOE_ACT_RELU2)
     }
   } else {
     MOE_TQ(2, 0)

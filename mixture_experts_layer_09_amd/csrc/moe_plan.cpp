@@ -52,12 +52,19 @@ void clear_error() { g_last_error.clear(); }
 
 const char* last_error() { return g_last_error.c_str(); }
 
+namespace {
+bool valid_act(int32_t act) {
+  return act == MOE_ACT_SILU_GATED || act == MOE_ACT_RELU2 || act == MOE_ACT_GELU_TANH_GATED;
+}
+bool is_gated(int32_t act) { return act != MOE_ACT_RELU2; }
+}  // namespace
+
 int32_t padded_intermediate(int32_t I, int32_t act, int32_t quant) {
-  if (act != MOE_ACT_SILU_GATED && act != MOE_ACT_RELU2) return MOE_ERR_INVALID_ARG;
+  if (!valid_act(act)) return MOE_ERR_INVALID_ARG;
   if (quant < MOE_QUANT_BF16 || quant > MOE_QUANT_W4A8) return MOE_ERR_INVALID_ARG;
   if (I <= 0) return MOE_ERR_INVALID_ARG;
   // the TRTLLM-Gen rule: 16 for gated, 128 for the non-gated relu2 path
-  int32_t a = act == MOE_ACT_SILU_GATED ? 16 : 128;
+  int32_t a = is_gated(act) ? 16 : 128;
   // what the kernels need: a bf16 MFMA k-step is 32 elements, an fp8 / int4
   // k-step, block scale and group scale cover 128
   int32_t k = quant == MOE_QUANT_BF16 ? 32 : 128;
@@ -66,7 +73,7 @@ int32_t padded_intermediate(int32_t I, int32_t act, int32_t quant) {
 }
 
 size_t packed_weight_bytes(const moe_problem& p, int which) {
-  const bool gated = p.act == MOE_ACT_SILU_GATED;
+  const bool gated = is_gated(p.act);
   const int64_t n = which == 13 ? (gated ? 2 * int64_t(p.I) : p.I) : p.H;
   const int64_t k = which == 13 ? p.H : p.I;
   const int64_t elems = int64_t(p.E) * n * k;
@@ -80,7 +87,7 @@ size_t packed_weight_bytes(const moe_problem& p, int which) {
 }
 
 size_t packed_scale_bytes(const moe_problem& p, int which) {
-  const bool gated = p.act == MOE_ACT_SILU_GATED;
+  const bool gated = is_gated(p.act);
   const int64_t n = which == 13 ? (gated ? 2 * int64_t(p.I) : p.I) : p.H;
   const int64_t k = which == 13 ? p.H : p.I;
   switch (p.quant) {
@@ -95,8 +102,9 @@ size_t packed_scale_bytes(const moe_problem& p, int which) {
 int make_plan(const moe_problem* p, Plan* plan) {
   char buf[256];
   if (!p || !plan) return fail(MOE_ERR_INVALID_ARG, "null problem");
-  if (p->act != MOE_ACT_SILU_GATED && p->act != MOE_ACT_RELU2)
-    return fail(MOE_ERR_INVALID_ARG, "act must be MOE_ACT_SILU_GATED or MOE_ACT_RELU2");
+  if (!valid_act(p->act))
+    return fail(MOE_ERR_INVALID_ARG,
+                "act must be MOE_ACT_SILU_GATED, MOE_ACT_RELU2 or MOE_ACT_GELU_TANH_GATED");
   if (p->quant < MOE_QUANT_BF16 || p->quant > MOE_QUANT_W4A8)
     return fail(MOE_ERR_INVALID_ARG, "unknown quant mode");
   if (p->T < 0 || p->H <= 0 || p->I <= 0)
@@ -128,7 +136,7 @@ int make_plan(const moe_problem* p, Plan* plan) {
   Plan q;
   q.Kp = p->top_k + p->n_shared;
   q.A = int64_t(p->T) * q.Kp;
-  q.gated = p->act == MOE_ACT_SILU_GATED;
+  q.gated = is_gated(p->act);
   q.N1 = q.gated ? 2 * p->I : p->I;
   const int64_t big = std::max<int64_t>(p->H, q.N1);
   if (q.A * big >= (int64_t(1) << 31))

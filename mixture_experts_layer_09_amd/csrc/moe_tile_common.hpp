@@ -18,7 +18,7 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
                                                int row0, int ct, int tile0, bool active,
                                                float* lds_amax) {
   constexpr int BM = NT * 16;
-  constexpr bool GATED = PHASE == 1 && ACT == MOE_ACT_SILU_GATED;
+  constexpr bool GATED = PHASE == 1 && act_gated(ACT);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4;
   const int mylane_row = lane & 15;
   if (PHASE == 1) {
@@ -36,7 +36,7 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (GATED) {
-            a[v][i] = silu(alpha * acc[2 * v][c][i]) * (alpha * acc[2 * v + 1][c][i]);
+            a[v][i] = gate_act<ACT>(alpha * acc[2 * v][c][i]) * (alpha * acc[2 * v + 1][c][i]);
           } else {
             const float h = fmaxf(alpha * acc[v][c][i], 0.f);
             a[v][i] = h * h;

@@ -50,7 +50,7 @@ def _st(lib, p):
 
 def test_valid_problems(plan):
     for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8"):
-        for a in ("silu", "relu2"):
+        for a in ("silu", "relu2", "gelu_tanh"):
             assert _st(plan, P(quant=q, act=a)) == moe.MOE_OK
     assert _st(plan, P(T=0)) == moe.MOE_OK
     assert _st(plan, P(n_shared=1, E_routed=8)) == moe.MOE_OK
@@ -63,11 +63,14 @@ def test_valid_problems(plan):
     (dict(top_k=0), moe.MOE_ERR_INVALID_ARG),
     (dict(top_k=9), moe.MOE_ERR_INVALID_ARG),
     (dict(act=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(act=3), moe.MOE_ERR_INVALID_ARG),
+    (dict(act=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(quant=9), moe.MOE_ERR_INVALID_ARG),
     (dict(block_m=17), moe.MOE_ERR_INVALID_ARG),
     (dict(block_m=256), moe.MOE_ERR_UNSUPPORTED),                 # 256: fp8 per-tensor, W4A8
     (dict(H=200), moe.MOE_ERR_ALIGNMENT),
     (dict(I=500), moe.MOE_ERR_ALIGNMENT),                       # gated bf16 needs 32
+    (dict(I=500, act="gelu_tanh"), moe.MOE_ERR_ALIGNMENT),
     (dict(I=96, act="relu2"), moe.MOE_ERR_ALIGNMENT),           # non-gated needs 128
     (dict(I=160, quant="fp8_tensor"), moe.MOE_ERR_ALIGNMENT),   # fp8 needs 128
     (dict(E_routed=1100, top_k=2), moe.MOE_ERR_UNSUPPORTED),    # > 1024 slots
@@ -96,6 +99,7 @@ def test_padded_intermediate(plan):
     f = plan.moe_padded_intermediate
     assert f(768, 0, 0) == 768 and f(1000, 0, 0) == 1024 and f(17, 0, 0) == 32
     assert f(2688, 1, 1) == 2688 and f(2600, 1, 0) == 2688 and f(100, 0, 2) == 128
+    assert f(1000, 2, 0) == 1024 and f(17, 2, 0) == 32 and f(100, 2, 2) == 128  # gelu_tanh: gated
     assert f(0, 0, 0) == moe.MOE_ERR_INVALID_ARG and f(10, 3, 0) == moe.MOE_ERR_INVALID_ARG
 
 
@@ -117,6 +121,7 @@ def test_capacity_bounds(plan, T, K, E):
 def test_packed_bytes(plan):
     w, s = ctypes.c_size_t(), ctypes.c_size_t()
     cases = [("bf16", "silu", 8 * 1024 * 256 * 2, 0), ("fp8_tensor", "relu2", 8 * 512 * 256, 32),
+             ("bf16", "gelu_tanh", 8 * 1024 * 256 * 2, 0),
              ("fp8_block", "silu", 8 * 1024 * 256, 8 * 8 * 2 * 4),
              ("w4a8", "silu", 8 * 1024 * 256 // 2, 8 * 1024 * 2 * 4)]
     for q, a, wb, sb in cases:

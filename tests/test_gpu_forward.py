@@ -53,7 +53,33 @@ def test_forward_config(cid, M, n):
     torch.cuda.empty_cache()
 
 
-SMALL = [(q, a) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8") for a in ("silu", "relu2")]
+# The gelu_tanh gate at full size: the decode shape (weight streaming) and
+# the fp8 block-scale prefill shape (8-wave LDS pipeline), same weights as
+# the SiLU configurations.
+GELU_FULL = [(2, 64, None), (3, 4096, 12)]
+
+
+@pytest.mark.parametrize("cid,M,n", GELU_FULL, ids=[f"cfg{c}-M{m}" for c, m, _ in GELU_FULL])
+def test_forward_gelu_tanh_full_size(cid, M, n):
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS[cid], act="gelu_tanh")
+    say(f"forward gelu_tanh {cfg.name} M={M} sample={n}")
+    W = weights_for(synth.CONFIGS[cid])
+    tok = synth.make_tokens(cfg, M)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
+    out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    rows = _sample(M, n, 7000 * cid + M)
+    ref = oracle_forward(cfg, W, tok["x_bits"][rows], tok["logits"][rows], sc["a1"], sc["a2"])
+    assert_close(got[rows], ref, cfg.quant, f"gelu_tanh {cfg.name} M={M}")
+    del layer
+    torch.cuda.empty_cache()
+
+
+SMALL = [(q, a) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
+         for a in ("silu", "relu2", "gelu_tanh")]
 
 
 @pytest.mark.parametrize("quant,act", SMALL)
@@ -180,8 +206,8 @@ def test_invalid_call_enqueues_nothing():
 
 
 TILED = [(q, a, bm) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
-         for a in ("silu", "relu2") for bm in (64, 128)] + \
-        [(q, a, 256) for q in ("fp8_tensor", "w4a8") for a in ("silu", "relu2")]
+         for a in ("silu", "relu2", "gelu_tanh") for bm in (64, 128)] + \
+        [(q, a, 256) for q in ("fp8_tensor", "w4a8") for a in ("silu", "relu2", "gelu_tanh")]
 
 
 @pytest.mark.parametrize("quant,act,bm", TILED)
@@ -203,8 +229,8 @@ def test_forward_tiled_ragged(quant, act, bm):
     assert_close(out.float().cpu().numpy(), ref, quant, f"tiled {quant} {act} bm={bm}")
 
 
-@pytest.mark.parametrize("quant,act", [("fp8_tensor", "silu"), ("fp8_tensor", "relu2"),
-                                       ("w4a8", "silu"), ("w4a8", "relu2")])
+@pytest.mark.parametrize("quant,act", [(q, a) for q in ("fp8_tensor", "w4a8")
+                                       for a in ("silu", "relu2", "gelu_tanh")])
 def test_forward_wide_blocks_by_default(quant, act):
     """fp8 per-tensor and int4 with 256+ rows per expert take 256-row blocks
     by themselves: several full blocks per expert, ragged last blocks, and
