@@ -14,6 +14,14 @@ TEST INFRASTRUCTURE (see the package docstring).
 * signed int4: two's complement in [-8, 7], two per byte, even k in the low
   nibble (the W4A8 page stores int4 weights with group scales; it does not
   print the nibble order, this is the reading taken).
+* OCP Microscaling (MX) formats, as the OCP MX specification v1.0 defines
+  them (the TRTLLM-Gen page names MXFP8 weights with one scale per 32 K
+  elements; the 4-bit weights of the pages are taken as MXFP4):
+  - E8M0 scale: 8 exponent bits, bias 127, no sign or mantissa; code c is
+    2^(c - 127); 0xFF is NaN;
+  - E2M1 element (FP4): 1 sign bit, 2 exponent bits with bias 1, 1 mantissa
+    bit; exponent field 0 is subnormal (m/2); magnitudes 0, 0.5, 1, 1.5, 2,
+    3, 4, 6; no NaN or infinity.  Two per byte, even k in the low nibble.
 """
 import numpy as np
 
@@ -99,4 +107,33 @@ def int4_unpack(packed):
     out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.int8)
     out[..., 0::2] = lo
     out[..., 1::2] = hi
+    return out
+
+
+def e8m0_decode(codes):
+    """E8M0 scale codes (uint8) -> float64 2^(c - 127); 0xFF -> NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c == 255, np.nan, np.exp2((c - 127).astype(np.float64)))
+
+
+def _e2m1_value(codes):
+    """The E2M1 value of each 4-bit code, from the field definitions."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = (c >> 3) & 1
+    exp = (c >> 1) & 0x3
+    man = c & 0x1
+    mag = np.where(exp == 0, man / 2.0, (1.0 + man / 2.0) * np.exp2(exp - 1.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+_E2M1_TABLE = _e2m1_value(np.arange(16))
+
+
+def e2m1_unpack_decode(packed):
+    """[..., K/2] uint8 of two E2M1 codes (even k in the low nibble) ->
+    [..., K] float64 values."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.float64)
+    out[..., 0::2] = _E2M1_TABLE[p & 0xF]
+    out[..., 1::2] = _E2M1_TABLE[p >> 4]
     return out

@@ -21,10 +21,13 @@ Steps, in the order the pages chain them:
 """
 import numpy as np
 
-from .codecs import (E4M3_MAX, bf16_decode, bf16_round, e4m3_decode,
-                     e4m3_encode, int4_unpack)
+from .codecs import (E4M3_MAX, bf16_decode, bf16_round, e2m1_unpack_decode,
+                     e4m3_decode, e4m3_encode, e8m0_decode, int4_unpack)
 
 GROUP = 128          # block / group width of the quantised formats
+MX_BLOCK = 32        # elements per E8M0 scale in the MX formats
+E4M3_EMAX = 8        # exponent of the largest e4m3 power of two (256 <= 448)
+MX_MODES = ("mxfp8", "mxfp4")
 
 
 # --------------------------------------------------------------------------
@@ -133,6 +136,31 @@ def quant_fp8_group(v, group=GROUP):
     return e4m3_encode(q).reshape(R, C), s
 
 
+def quant_mx8(v):
+    """MXFP8 (OCP MX v1.0, conversion of a vector to an MX block): per row
+    and per 32 consecutive columns, the shared exponent is
+    X = floor(log2(amax)) - 8 (8: the e4m3 emax), kept in [-127, 127], and
+    X = -127 for an all-zero block; each element is e4m3(fp32(v) / 2^X),
+    nearest even, saturating at 448 (the clamp the specification prescribes
+    for magnitudes above the largest normal).
+
+    Returns (codes uint8 [R, C], scale codes uint8 [R, C/32] = X + 127).
+    """
+    f = np.asarray(v, dtype=np.float32)
+    R, C = f.shape
+    g = f.reshape(R, C // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    amax = np.abs(g).max(axis=-1)
+    _, ex = np.frexp(amax)                 # amax = m 2^ex, m in [0.5, 1)
+    X = np.where(amax > 0, ex - 1 - E4M3_EMAX, -127)
+    X = np.clip(X, -127, 127).astype(np.int64)
+    q = (g * np.exp2(-X.astype(np.float64))[..., None]).astype(np.float32)
+    return e4m3_encode(q).reshape(R, C), (X + 127).astype(np.uint8)
+
+
+def _mx_scale_full(scale_codes, cols):
+    return np.repeat(e8m0_decode(scale_codes), MX_BLOCK, axis=-1)[..., :cols]
+
+
 def quant_x(x, quant, a1=None):
     """Step a3: the activations as the GEMM1 operand.
 
@@ -146,6 +174,8 @@ def quant_x(x, quant, a1=None):
         return quant_fp8_tensor(x, a1), None
     if quant == "fp8_block":
         return quant_fp8_group(x)
+    if quant in MX_MODES:
+        return quant_mx8(x)
     raise ValueError(quant)
 
 
@@ -156,6 +186,8 @@ def dequant_x(x, quant, codes, scales, a1=None):
         return e4m3_decode(codes) * float(np.float32(a1))
     if quant == "fp8_block":
         return e4m3_decode(codes) * np.repeat(scales.astype(np.float64), GROUP, axis=1)
+    if quant in MX_MODES:
+        return e4m3_decode(codes) * _mx_scale_full(scales, codes.shape[1])
     raise ValueError(quant)
 
 
@@ -239,6 +271,13 @@ def _dequant(codes, scale, quant, e, row_origin=None):
         rows = np.arange(n) if row_origin is None else row_origin
         s = bf16_decode(scale[e])[rows]                          # [n, K/128]
         return q * np.repeat(s, GROUP, axis=1)[:, :k]
+    if quant in MX_MODES:
+        # MX weights: one E8M0 scale per row per 32 K (TRTLLM-Gen page,
+        # _align_mxfp8_moe_weights: scales [E, rows, K/32])
+        w = e4m3_decode(codes[e]) if quant == "mxfp8" else e2m1_unpack_decode(codes[e])
+        n, k = w.shape
+        rows = np.arange(n) if row_origin is None else row_origin
+        return w * _mx_scale_full(scale[e][rows], k)
     raise ValueError(quant)
 
 
@@ -267,7 +306,8 @@ def store_intermediate(a, quant, a2=None):
 
     bf16: fp32 then bf16 (nearest even).  fp8_tensor / w4a8: e4m3 of
     fp32(a)/a2, saturating, times a2.  fp8_block: per row and 128 columns,
-    s = fp32(amax/448), e4m3 of fp32(a)/s, times s.  "exact": unchanged.
+    s = fp32(amax/448), e4m3 of fp32(a)/s, times s.  mxfp8 / mxfp4: MXFP8 per
+    row and 32 columns (quant_mx8).  "exact": unchanged.
     """
     if quant == "exact":
         return a
@@ -278,6 +318,9 @@ def store_intermediate(a, quant, a2=None):
     if quant == "fp8_block":
         q, s = quant_fp8_group(a)
         return e4m3_decode(q) * np.repeat(s.astype(np.float64), GROUP, axis=1)
+    if quant in MX_MODES:
+        q, s = quant_mx8(a)
+        return e4m3_decode(q) * _mx_scale_full(s, q.shape[1])
     raise ValueError(quant)
 
 
@@ -305,8 +348,14 @@ def flip_margin(a, quant, a2=None):
     elif quant == "fp8_block":
         _, sg = quant_fp8_group(a)
         s = np.repeat(sg.astype(np.float64), GROUP, axis=1)
+    elif quant in MX_MODES:
+        return _flip_margin_mx(a)
     else:
         return np.zeros_like(a)
+    return _flip_margin_at(a, s)
+
+
+def _flip_margin_at(a, s):
     q = np.abs(a / s)
     pos = e4m3_decode(np.arange(127, dtype=np.uint8))        # 0 .. 448, increasing
     mids = (pos[1:] + pos[:-1]) / 2.0                        # boundary i: pos[i] | pos[i+1]
@@ -403,3 +452,33 @@ def moe_forward(x, w13, w2, *, quant, act, E_routed, top_k, renormalize,
     if with_margin:
         res["margin"] = margin
     return res
+
+
+def _flip_margin_mx(a):
+    """flip_margin for the MXFP8 intermediate.  Each element's rounding as
+    above, at its block's scale 2^X.  In addition, where the block's amax lies
+    within FLIP_REL (relative) of a power of two, fp32 accumulation may put
+    it on either side, and the block may take the exponent X or its
+    neighbour: there each element's margin also covers the change between its
+    values under the two exponents plus one e4m3 step at the coarser one."""
+    R, C = a.shape
+    nb = C // MX_BLOCK
+    q, sc = quant_mx8(a)
+    m = _flip_margin_at(a, _mx_scale_full(sc, C))
+    f = np.asarray(a, dtype=np.float32).astype(np.float64).reshape(R, nb, MX_BLOCK)
+    amax = np.abs(f).max(axis=-1)
+    lg = np.log2(np.where(amax > 0, amax, 1.0))
+    n = np.round(lg)
+    near = (amax > 0) & (np.abs(amax / np.exp2(n) - 1.0) <= FLIP_REL)
+    if not near.any():
+        return m
+    X = sc.astype(np.int64) - 127
+    X2 = np.clip(np.where(lg < n, X + 1, X - 1), -127, 127)   # the neighbouring exponent
+    v1 = e4m3_decode(q).reshape(R, nb, MX_BLOCK) * np.exp2(X)[..., None]
+    q2 = e4m3_encode((f * np.exp2(-X2.astype(np.float64))[..., None]).astype(np.float32))
+    v2 = e4m3_decode(q2) * np.exp2(X2)[..., None]
+    Xc = np.maximum(X, X2)[..., None].astype(np.float64)
+    qc = np.abs(f) * np.exp2(-Xc)
+    step = np.exp2(np.floor(np.log2(np.maximum(qc, 2.0 ** -6))) - 3.0) * np.exp2(Xc)
+    extra = np.where(near[..., None], np.abs(v1 - v2) + step, 0.0).reshape(R, C)
+    return np.maximum(m, extra)

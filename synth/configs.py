@@ -25,7 +25,7 @@ class MoEConfig:
     n_shared: int     # shared-expert slots appended after the routed ones
     shared_gate: float
     act: str          # "silu" / "gelu_tanh" (gated: act(gate)*up) or "relu2" (relu(x)^2)
-    quant: str        # "bf16" | "fp8_tensor" | "fp8_block" | "w4a8"
+    quant: str        # "bf16" | "fp8_tensor" | "fp8_block" | "w4a8" | "mxfp8" | "mxfp4"
     renormalize: bool
     Ms: Tuple[int, ...]
     a2_const: float = 0.0   # static intermediate activation scale (fp8 / w4a8)

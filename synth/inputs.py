@@ -11,7 +11,12 @@ regenerated on its own):
    - fp8 e4m3 with one fp32 scale per expert (scale = amax / 448),
    - fp8 e4m3 with one fp32 scale per 128x128 block, scale ~ U(0.5, 2) / 64,
    - signed int4 with one bf16 scale per 128 consecutive K (scale = amax/7),
-     packed two per byte, even k in the low nibble.
+     packed two per byte, even k in the low nibble,
+   - MXFP8: e4m3 codes with one E8M0 scale per row per 32 K, the scale
+     2^(floor(log2 amax) - 8) of the 32 values (torch's e4m3 cast, clamped),
+   - MXFP4: E2M1 codes (nearest of the 16 values) with one E8M0 scale per
+     row per 32 K, 2^(floor(log2 amax) - 2), packed two per byte, even k in
+     the low nibble.
  * static activation scales for the per-tensor modes: a1 = amax(x) / 448 and
    a fixed a2 per configuration.
 
@@ -66,6 +71,24 @@ def _pack_int4(q: np.ndarray) -> np.ndarray:
     return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
 
 
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def _mx_exponent(w: np.ndarray, emax: int) -> np.ndarray:
+    """Per row and 32 K: floor(log2 amax) - emax (-127 for an all-zero block)."""
+    n, k = w.shape
+    amax = np.abs(w.reshape(n, k // 32, 32)).max(axis=-1).astype(np.float64)
+    _, ex = np.frexp(amax)
+    return np.clip(np.where(amax > 0, ex - 1 - emax, -127), -127, 127).astype(np.int64)
+
+
+def _to_e2m1_codes(v: np.ndarray) -> np.ndarray:
+    """float -> 4-bit E2M1 codes: the nearest magnitude of the table, sign bit 3."""
+    mag = np.abs(v)[..., None]
+    idx = np.argmin(np.abs(mag - _E2M1_MAG), axis=-1).astype(np.uint8)
+    return idx | ((np.signbit(v) & (idx > 0)).astype(np.uint8) << 3)
+
+
 def _workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -96,6 +119,16 @@ def _gen_expert(cfg: MoEConfig, seed: int, which: int, e: int):
         s = bf16_bits_to_f32(s_bits)
         qv = np.clip(np.rint(g / s[..., None]), -8, 7).astype(np.int8).reshape(n, k)
         return _pack_int4(qv), s_bits
+    if q in ("mxfp8", "mxfp4"):
+        emax = 8 if q == "mxfp8" else 2
+        X = _mx_exponent(w, emax)
+        full = np.repeat(np.exp2(-X.astype(np.float64)), 32, axis=1)
+        scaled = (w.astype(np.float64) * full).astype(np.float32)
+        sc = (X + 127).astype(np.uint8)
+        if q == "mxfp8":
+            return to_e4m3_codes(scaled), sc
+        c = _to_e2m1_codes(scaled)
+        return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8), sc
     raise ValueError(q)
 
 
