@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the fused MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload cfg2_M64] [--act A] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload cfg2_M64] [--act A] [--quant Q]
+                    [--gpus 1]
 
 One step is one whole pass of the layer -- route + (fp8 quantise) + align,
 GEMM1 + activation, GEMM2 + combine -- over one batch of synthetic tokens
@@ -44,6 +45,9 @@ def parse():
     ap.add_argument("--workload", default="cfg2_M64")
     ap.add_argument("--act", choices=("silu", "relu2", "gelu_tanh"), default=None,
                     help="replace the workload's activation (same shapes otherwise)")
+    ap.add_argument("--quant", default=None,
+                    choices=("bf16", "fp8_tensor", "fp8_block", "w4a8", "mxfp8", "mxfp4"),
+                    help="replace the workload's weight format (same shapes otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -82,7 +86,8 @@ def make_layer(cfg, W, a1, a2):
 
 
 def weight_bytes_per_expert(cfg):
-    el = {"bf16": 2.0, "fp8_tensor": 1.0, "fp8_block": 1.0, "w4a8": 0.5}[cfg.quant]
+    el = {"bf16": 2.0, "fp8_tensor": 1.0, "fp8_block": 1.0, "w4a8": 0.5, "mxfp8": 1.0,
+          "mxfp4": 0.5}[cfg.quant]
     w13 = cfg.N1 * cfg.H * el
     w2 = cfg.H * cfg.I * el
     if cfg.quant == "fp8_block":
@@ -94,6 +99,9 @@ def weight_bytes_per_expert(cfg):
     elif cfg.quant == "fp8_tensor":
         w13 += 4
         w2 += 4
+    elif cfg.quant in ("mxfp8", "mxfp4"):
+        w13 += cfg.N1 * cfg.H // 32        # one E8M0 byte per 32 weights
+        w2 += cfg.H * cfg.I // 32
     return w13, w2
 
 
@@ -235,7 +243,11 @@ def main():
     if args.act is not None and args.act != cfg.act:
         import dataclasses
         cfg = dataclasses.replace(cfg, act=args.act)
-        key = f"{args.workload}_{args.act}"
+        key = f"{key}_{args.act}"
+    if args.quant is not None and args.quant != cfg.quant:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, quant=args.quant)
+        key = f"{key}_{args.quant}"
     W = synth.make_weights(cfg)
     tok = synth.make_tokens(cfg, M)
     sc = synth.make_act_scales(cfg, tok["x_bits"])
@@ -274,7 +286,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.quant == "bf16" else ("fp8" if cfg.quant != "w4a8" else "int4xfp8"),
+        "dtype": {"bf16": "bf16", "w4a8": "int4xfp8", "mxfp8": "mxfp8",
+                  "mxfp4": "mxfp4xmxfp8"}.get(cfg.quant, "fp8"),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} M={M}: hidden {cfg.H}, {cfg.E_routed} routed "
                                f"+ {cfg.n_shared} shared experts, top-{cfg.top_k}, "

@@ -99,9 +99,19 @@ enum moe_quant {
                                block; e4m3 activations with one fp32 scale per
                                token per 128 columns, computed on the fly
                                [SHARED]                                         */
-  MOE_QUANT_W4A8 = 3        /* signed int4 weights with one bf16 scale per row
+  MOE_QUANT_W4A8 = 3,       /* signed int4 weights with one bf16 scale per row
                                per 128 K; e4m3 activations with static a1, a2
                                [W4A8]                                           */
+  MOE_QUANT_MXFP8 = 4,      /* OCP MX: e4m3 weights with one E8M0 scale per row
+                               per 32 K ([TRTLLM] section 2,
+                               _align_mxfp8_moe_weights: scales [E, N, K/32]);
+                               x and the intermediate quantised to MXFP8 on
+                               the fly (E8M0 per token per 32 columns)          */
+  MOE_QUANT_MXFP4 = 5       /* OCP MX: E2M1 (fp4) weights, two per byte with the
+                               even k in the low nibble, one E8M0 scale per row
+                               per 32 K; activations MXFP8 as for MOE_QUANT_MXFP8
+                               (the 4-bit weights of [TRTLLM] section 3 and
+                               [GATED], taken as MXFP4)                         */
 };
 
 /* Shape and mode of one layer call. */
@@ -121,7 +131,8 @@ typedef struct moe_problem {
   int32_t quant;        /* enum moe_quant                                        */
   int32_t block_m;      /* alignment block (rows per GEMM tile): 0 = library
                            choice, else 16, 64, 128 or 256 (256: fp8
-                           per-tensor and W4A8 modes only).  Every call of one
+                           per-tensor and W4A8 modes only; the MX modes run
+                           16 and 128).  Every call of one
                            layer pass must see the same resolved value
                            (moe_block_m).                                        */
 } moe_problem;
@@ -130,8 +141,8 @@ typedef struct moe_problem {
 typedef struct moe_weights {
   const void* w13;        /* packed up-projection                              */
   const void* w2;         /* packed down-projection                            */
-  const float* w13_scale; /* packed scales (moe_packed_bytes); NULL for bf16   */
-  const float* w2_scale;  /* packed scales; NULL for bf16                       */
+  const void* w13_scale;  /* packed scales (moe_packed_bytes); NULL for bf16   */
+  const void* w2_scale;   /* packed scales; NULL for bf16                       */
   const float* a1_scale;  /* [1] static x scale: FP8_TENSOR, W4A8; else NULL   */
   const float* a2_scale;  /* [1] static intermediate scale: FP8_TENSOR, W4A8    */
 } moe_weights;
@@ -185,11 +196,14 @@ int moe_packed_bytes(const moe_problem* p, int32_t which, size_t* w_bytes,
  *               rows first, or up rows first when swap_halves = 1) or src_I
  *               (non-gated).  Elements: bf16 bits (BF16), e4m3 codes (FP8_*),
  *               or int4 packed two per byte with the even k in the low nibble
- *               ([E][N1s][H/2], W4A8).
+ *               ([E][N1s][H/2], W4A8), e4m3 codes (MXFP8), E2M1 codes two per
+ *               byte, even k in the low nibble ([E][N1s][H/2], MXFP4).
  *   src_I     : unpadded intermediate size, src_I <= p->I; rows src_I..I-1 of
- *               each half are zero-filled (FP8_BLOCK and W4A8 need src_I == I).
+ *               each half are zero-filled (FP8_BLOCK and W4A8 need src_I == I,
+ *               the MX modes a multiple of 32).
  *   src_scale : FP8_TENSOR fp32 [E]; FP8_BLOCK fp32 [E][N1s/128][H/128];
- *               W4A8 bf16 bits [E][N1s][H/128]; NULL for BF16.
+ *               W4A8 bf16 bits [E][N1s][H/128]; MXFP8 / MXFP4 E8M0 bytes
+ *               [E][N1s][H/32]; NULL for BF16.
  *   dst       : moe_packed_bytes(p, 13) bytes; gate/up rows interleaved in
  *               groups of 16 and pre-tiled in the MFMA operand order.
  *   dst_scale : the packed scales (moe_packed_bytes(p, 13) scale bytes).
@@ -198,9 +212,11 @@ int moe_pack_w13(const moe_problem* p, const void* src, int32_t src_I,
                  int32_t swap_halves, const void* src_scale, void* dst,
                  void* dst_scale, moe_stream_t stream);
 
-/* Load-time packing of the down-projection: src [E][H][src_I] (int4:
+/* Load-time packing of the down-projection: src [E][H][src_I] (int4, fp4:
  * [E][H][src_I/2]), scales FP8_TENSOR [E], FP8_BLOCK [E][H/128][src_I/128],
- * W4A8 bf16 [E][H][src_I/128]; columns src_I..I-1 are zero-filled. */
+ * W4A8 bf16 [E][H][src_I/128], MX E8M0 bytes [E][H][src_I/32]; columns
+ * src_I..I-1 are zero-filled (the scale padding of [TRTLLM] section 2,
+ * _align_mxfp8_moe_weights). */
 int moe_pack_w2(const moe_problem* p, const void* src, int32_t src_I,
                 const void* src_scale, void* dst, void* dst_scale,
                 moe_stream_t stream);
@@ -242,18 +258,22 @@ int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* sorted_ids
  * of x -- quantise in one kernel launch; larger ones run the separate
  * kernels.  Outputs are bit-identical to the separate calls. */
 int moe_prepare(const moe_problem* p, const float* logits, int32_t* topk_ids, float* topk_w,
-                const uint16_t* x, const float* a1_scale, uint8_t* xq, float* x_scale,
+                const uint16_t* x, const float* a1_scale, uint8_t* xq, void* x_scale,
                 int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
                 int32_t* num_padded, void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* fp8 activation quantisation of x (bf16 [T][H]) for the fp8 and W4A8 modes:
+/* fp8 activation quantisation of x (bf16 [T][H]) for the fp8, W4A8 and MX modes:
  *   FP8_TENSOR, W4A8 : xq = e4m3(sat(x / a1)), x_scale unused (may be NULL);
  *   FP8_BLOCK        : per token and 128 columns s = amax/448 (1 if amax = 0),
- *                      xq = e4m3(x / s), x_scale fp32 [T][H/128] = s.
+ *                      xq = e4m3(x / s), x_scale fp32 [T][H/128] = s;
+ *   MXFP8, MXFP4     : MXFP8 per token and 32 columns (OCP MX v1.0): shared
+ *                      exponent X = floor(log2 amax) - 8 in [-127, 127]
+ *                      (-127 if amax = 0), xq = e4m3(sat(x / 2^X)), x_scale
+ *                      E8M0 bytes [T][H/32] = X + 127.
  * Division is IEEE fp32; e4m3 rounds to nearest even and saturates at 448.
  * a1_scale is a device pointer to one float (FP8_TENSOR, W4A8). */
 int moe_quant_act(const moe_problem* p, const uint16_t* x, const float* a1_scale,
-                  uint8_t* xq, float* x_scale, moe_stream_t stream);
+                  uint8_t* xq, void* x_scale, moe_stream_t stream);
 
 /* Grouped GEMM1 with the activation in the epilogue ([SWIGLU] sections 1-2;
  * [GATED] section 2).  For every padded row r < *num_padded of block
@@ -262,16 +282,19 @@ int moe_quant_act(const moe_problem* p, const uint16_t* x, const float* a1_scale
  *                              unspecified but finite values)
  *   a = SiLU(h_gate) * h_up  or  relu(h)^2, after dequantisation
  *   a2[r][:] = a in the compute format: bf16 (BF16), e4m3(sat(a / a2))
- *   (FP8_TENSOR, W4A8), or per 128 columns e4m3(a / s) with s = amax/448
- *   written to a2_scale [rows][I/128] (FP8_BLOCK).
+ *   (FP8_TENSOR, W4A8), per 128 columns e4m3(a / s) with s = amax/448
+ *   written to a2_scale fp32 [rows][I/128] (FP8_BLOCK), or MXFP8 per 32
+ *   columns as in moe_quant_act with the E8M0 bytes in a2_scale [rows][I/32]
+ *   (MXFP8, MXFP4).
  *   x       : bf16 [T][H] (BF16) or e4m3 codes [T][H] (moe_quant_act).
- *   x_scale : fp32 [T][H/128] for FP8_BLOCK, else ignored.
+ *   x_scale : fp32 [T][H/128] for FP8_BLOCK, E8M0 [T][H/32] for the MX modes,
+ *             else ignored.
  *   a2      : [moe_max_padded_rows][I] bf16 or e4m3.
  * The full-width h is never written to memory. */
-int moe_gemm1_act(const moe_problem* p, const void* x, const float* x_scale,
+int moe_gemm1_act(const moe_problem* p, const void* x, const void* x_scale,
                   const moe_weights* w, const int32_t* sorted_ids,
                   const int32_t* block_expert, const int32_t* num_padded,
-                  void* a2, float* a2_scale, moe_stream_t stream);
+                  void* a2, void* a2_scale, moe_stream_t stream);
 
 /* Grouped GEMM2 and the routing-weighted combine ([GATED] sections 3-4:
  * FC2 non-gated, scatter unchanged; [TRTLLM]: bf16 output of x's shape).
@@ -281,7 +304,7 @@ int moe_gemm1_act(const moe_problem* p, const void* x, const float* x_scale,
  *             summed in slot order j = 0..K'-1, rounded once
  * out is written completely (rows with no valid slot become 0).
  *   y_ws   : moe_combine_workspace_bytes(p) bytes of scratch. */
-int moe_gemm2_combine(const moe_problem* p, const void* a2, const float* a2_scale,
+int moe_gemm2_combine(const moe_problem* p, const void* a2, const void* a2_scale,
                       const moe_weights* w, const int32_t* sorted_ids,
                       const int32_t* block_expert, const int32_t* num_padded,
                       const int32_t* topk_ids, const float* topk_w, void* y_ws,

@@ -18,7 +18,7 @@ PLAN_LIB_PATH = os.path.join(HERE, "libmoe_plan.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED = 0, -1, -2
 MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = -3, -4, -5
 ACT = {"silu": 0, "relu2": 1, "gelu_tanh": 2}
-QUANT = {"bf16": 0, "fp8_tensor": 1, "fp8_block": 2, "w4a8": 3}
+QUANT = {"bf16": 0, "fp8_tensor": 1, "fp8_block": 2, "w4a8": 3, "mxfp8": 4, "mxfp4": 5}
 
 # every entry point declared in include/moe.h
 EXPORTS = (

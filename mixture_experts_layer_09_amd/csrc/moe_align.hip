@@ -197,10 +197,11 @@ struct PrologueArgs {
   const uint16_t* x;       // quantisation (QM != 0)
   const float* a1;
   uint8_t* xq;
-  float* xs;
+  void* xs;                // fp32 (QM 2) or E8M0 bytes (QM 3)
 };
 
-// QM: 0 no quantisation, 1 static per-tensor a1, 2 per token and 128 columns.
+// QM: 0 no quantisation, 1 static per-tensor a1, 2 per token and 128 columns,
+// 3 MXFP8 per token and 32 columns.
 template <int L, int NPL, int QM>
 __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
   extern __shared__ int smem[];
@@ -249,9 +250,23 @@ __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
         amax = fmaxf(amax, fmaxf(fabsf(f[2 * k]), fabsf(f[2 * k + 1])));
       }
       float s = s1;
-      if (QM == 2) {
+      if (QM >= 2) {
         amax = fmaxf(amax, __uint_as_float(dpp<kDppXor1, 0xF>(0u, __float_as_uint(amax))));
         amax = fmaxf(amax, __uint_as_float(dpp<kDppXor2, 0xF>(0u, __float_as_uint(amax))));
+      }
+      if (QM == 3) {
+        // 4 lanes (a DPP quad) are one 32-column block
+        const int X = mx8_exponent(amax);
+        if (in) {
+          u32x2 o;
+          o[0] = mx8x4(f[0], f[1], f[2], f[3], X);
+          o[1] = mx8x4(f[4], f[5], f[6], f[7], X);
+          *reinterpret_cast<u32x2*>(a.xq + size_t(i) * 8) = o;
+          if ((threadIdx.x & 3) == 0) static_cast<uint8_t*>(a.xs)[i / 4] = uint8_t(X + 127);
+        }
+        continue;
+      }
+      if (QM == 2) {
         amax = fmaxf(amax, __uint_as_float(dpp<kDppHalfMirror, 0xF>(0u, __float_as_uint(amax))));
         amax = fmaxf(amax, __uint_as_float(dpp<kDppMirror, 0xF>(0u, __float_as_uint(amax))));
         s = amax > 0.f ? amax / 448.f : 1.f;
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
         o[0] = e4m3x4(f[0], f[1], f[2], f[3]);
         o[1] = e4m3x4(f[4], f[5], f[6], f[7]);
         *reinterpret_cast<u32x2*>(a.xq + size_t(i) * 8) = o;
-        if (QM == 2 && (threadIdx.x & 15) == 0) a.xs[i / 16] = s;
+        if (QM == 2 && (threadIdx.x & 15) == 0) static_cast<float*>(a.xs)[i / 16] = s;
       }
     }
   }
@@ -475,7 +490,7 @@ bool prologue_fits(const moe_problem& p, const Plan& q) {
 
 hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* logits,
                            int32_t* ids, float* w, const uint16_t* x, const float* a1,
-                           uint8_t* xq, float* xs, bool quantise, int32_t* sorted_ids,
+                           uint8_t* xq, void* xs, bool quantise, int32_t* sorted_ids,
                            int32_t* block_expert, int32_t* offsets, int32_t* num_padded,
                            int32_t* scratch, hipStream_t stream) {
   // The single-workgroup prologue quantises x in passes of one 8-element
@@ -521,6 +536,7 @@ hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* log
   const size_t sm = size_t(kThreads) * 4 + small_tables_bytes(p.E);
   if (!quantise) return prologue_q<0>(p, a, sm, stream);
   if (p.quant == MOE_QUANT_FP8_BLOCK) return prologue_q<2>(p, a, sm, stream);
+  if (quant_is_mx(p.quant)) return prologue_q<3>(p, a, sm, stream);
   return prologue_q<1>(p, a, sm, stream);
 }
 

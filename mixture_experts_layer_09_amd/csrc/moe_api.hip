@@ -24,6 +24,21 @@ bool fp8_static(int quant) {
   return quant == MOE_QUANT_FP8_TENSOR || quant == MOE_QUANT_W4A8;
 }
 
+// Modes whose activations carry scales computed on the fly (x_scale, a2_scale).
+bool dynamic_scales(int quant) {
+  return quant == MOE_QUANT_FP8_BLOCK || moe::quant_is_mx(quant);
+}
+
+// Source intermediate sizes the packers take for the mode.
+int check_src_I(const moe_problem& p, int32_t src_I) {
+  if (src_I < 1 || src_I > p.I) return moe::fail(MOE_ERR_INVALID_ARG, "need 1 <= src_I <= I");
+  if ((p.quant == MOE_QUANT_FP8_BLOCK || p.quant == MOE_QUANT_W4A8) && src_I != p.I)
+    return moe::fail(MOE_ERR_ALIGNMENT, "block / group scaled weights need src_I == I");
+  if (moe::quant_is_mx(p.quant) && src_I % 32 != 0)
+    return moe::fail(MOE_ERR_ALIGNMENT, "MX weights need src_I to be a multiple of 32");
+  return MOE_OK;
+}
+
 // Pointer checks shared by the GEMM entry points.
 int check_weights(const moe_problem& p, const moe_weights* w, int which) {
   if (!w) return null_arg("weights");
@@ -50,9 +65,7 @@ int moe_pack_w13(const moe_problem* p, const void* src, int32_t src_I, int32_t s
   moe::Plan q;
   int st = moe::make_plan(p, &q);
   if (st != MOE_OK) return st;
-  if (src_I < 1 || src_I > p->I) return moe::fail(MOE_ERR_INVALID_ARG, "need 1 <= src_I <= I");
-  if ((p->quant == MOE_QUANT_FP8_BLOCK || p->quant == MOE_QUANT_W4A8) && src_I != p->I)
-    return moe::fail(MOE_ERR_ALIGNMENT, "block / group scaled weights need src_I == I");
+  if ((st = check_src_I(*p, src_I)) != MOE_OK) return st;
   if (swap_halves != 0 && swap_halves != 1)
     return moe::fail(MOE_ERR_INVALID_ARG, "swap_halves must be 0 or 1");
   if (!src) return null_arg("src");
@@ -70,9 +83,7 @@ int moe_pack_w2(const moe_problem* p, const void* src, int32_t src_I, const void
   moe::Plan q;
   int st = moe::make_plan(p, &q);
   if (st != MOE_OK) return st;
-  if (src_I < 1 || src_I > p->I) return moe::fail(MOE_ERR_INVALID_ARG, "need 1 <= src_I <= I");
-  if ((p->quant == MOE_QUANT_FP8_BLOCK || p->quant == MOE_QUANT_W4A8) && src_I != p->I)
-    return moe::fail(MOE_ERR_ALIGNMENT, "block / group scaled weights need src_I == I");
+  if ((st = check_src_I(*p, src_I)) != MOE_OK) return st;
   if (!src) return null_arg("src");
   if (!dst) return null_arg("dst");
   if (p->quant != MOE_QUANT_BF16 && (!src_scale || !dst_scale)) return null_arg("scale");
@@ -125,7 +136,7 @@ int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* sorted_ids
 }
 
 int moe_prepare(const moe_problem* p, const float* logits, int32_t* topk_ids, float* topk_w,
-                const uint16_t* x, const float* a1_scale, uint8_t* xq, float* x_scale,
+                const uint16_t* x, const float* a1_scale, uint8_t* xq, void* x_scale,
                 int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
                 int32_t* num_padded, void* ws, size_t ws_bytes, moe_stream_t stream) {
   moe::clear_error();
@@ -144,7 +155,7 @@ int moe_prepare(const moe_problem* p, const float* logits, int32_t* topk_ids, fl
     if (!block_expert) return null_arg("block_expert");
     if (quantise) {
       if (!xq) return null_arg("xq");
-      if (p->quant == MOE_QUANT_FP8_BLOCK && !x_scale) return null_arg("x_scale");
+      if (dynamic_scales(p->quant) && !x_scale) return null_arg("x_scale");
       if (fp8_static(p->quant) && !a1_scale) return null_arg("a1_scale");
     }
   }
@@ -166,26 +177,26 @@ int moe_prepare(const moe_problem* p, const float* logits, int32_t* topk_ids, fl
 }
 
 int moe_quant_act(const moe_problem* p, const uint16_t* x, const float* a1_scale, uint8_t* xq,
-                  float* x_scale, moe_stream_t stream) {
+                  void* x_scale, moe_stream_t stream) {
   moe::clear_error();
   moe::Plan q;
   int st = moe::make_plan(p, &q);
   if (st != MOE_OK) return st;
   if (p->quant == MOE_QUANT_BF16)
-    return moe::fail(MOE_ERR_INVALID_ARG, "moe_quant_act applies to the fp8 and W4A8 modes");
+    return moe::fail(MOE_ERR_INVALID_ARG, "moe_quant_act applies to the fp8, W4A8 and MX modes");
   if (p->T == 0) return MOE_OK;
   if (!x) return null_arg("x");
   if (!xq) return null_arg("xq");
-  if (p->quant == MOE_QUANT_FP8_BLOCK && !x_scale) return null_arg("x_scale");
+  if (dynamic_scales(p->quant) && !x_scale) return null_arg("x_scale");
   if (fp8_static(p->quant) && !a1_scale) return null_arg("a1_scale");
   clear_stale_launch_error();
   return hip_status(moe::launch_quant_act(*p, x, a1_scale, xq, x_scale, (hipStream_t)stream),
                     "moe_quant_act");
 }
 
-int moe_gemm1_act(const moe_problem* p, const void* x, const float* x_scale,
+int moe_gemm1_act(const moe_problem* p, const void* x, const void* x_scale,
                   const moe_weights* w, const int32_t* sorted_ids, const int32_t* block_expert,
-                  const int32_t* num_padded, void* a2, float* a2_scale, moe_stream_t stream) {
+                  const int32_t* num_padded, void* a2, void* a2_scale, moe_stream_t stream) {
   moe::clear_error();
   moe::Plan q;
   int st = moe::make_plan(p, &q);
@@ -197,7 +208,7 @@ int moe_gemm1_act(const moe_problem* p, const void* x, const float* x_scale,
   if (!block_expert) return null_arg("block_expert");
   if (!num_padded) return null_arg("num_padded");
   if (!a2) return null_arg("a2");
-  if (p->quant == MOE_QUANT_FP8_BLOCK) {
+  if (dynamic_scales(p->quant)) {
     if (!x_scale) return null_arg("x_scale");
     if (!a2_scale) return null_arg("a2_scale");
   }
@@ -207,7 +218,7 @@ int moe_gemm1_act(const moe_problem* p, const void* x, const float* x_scale,
                     "moe_gemm1_act");
 }
 
-int moe_gemm2_combine(const moe_problem* p, const void* a2, const float* a2_scale,
+int moe_gemm2_combine(const moe_problem* p, const void* a2, const void* a2_scale,
                       const moe_weights* w, const int32_t* sorted_ids,
                       const int32_t* block_expert, const int32_t* num_padded,
                       const int32_t* topk_ids, const float* topk_w, void* y_ws,
@@ -225,7 +236,7 @@ int moe_gemm2_combine(const moe_problem* p, const void* a2, const float* a2_scal
   if (!block_expert) return null_arg("block_expert");
   if (!num_padded) return null_arg("num_padded");
   if (!topk_w) return null_arg("topk_w");
-  if (p->quant == MOE_QUANT_FP8_BLOCK && !a2_scale) return null_arg("a2_scale");
+  if (dynamic_scales(p->quant) && !a2_scale) return null_arg("a2_scale");
   if (!y_ws) return null_arg("y_ws");
   if (y_ws_bytes < q.combine_ws) return moe::fail(MOE_ERR_WORKSPACE, "y workspace too small");
   float* y = static_cast<float*>(y_ws);
@@ -267,9 +278,9 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const uint16_t* x,
   int32_t* npad = reinterpret_cast<int32_t*>(base + q.off_npad);
   int32_t* scratch = reinterpret_cast<int32_t*>(base + q.off_align);
   uint8_t* xq = base + q.off_xq;
-  float* xs = reinterpret_cast<float*>(base + q.off_xs);
+  void* xs = base + q.off_xs;
   void* a2 = base + q.off_a2;
-  float* a2s = reinterpret_cast<float*>(base + q.off_a2s);
+  void* a2s = base + q.off_a2s;
   float* y = reinterpret_cast<float*>(base + q.off_y);
   hipStream_t s = (hipStream_t)stream;
   clear_stale_launch_error();

@@ -25,6 +25,18 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 }
 
 // ---------------------------------------------------------------- MFMA
+// D[16x16] += A[16x128] * B[128x16] with one E8M0 scale per row / column and
+// 32 k (the OCP MX block): the scale of row (A) or column (B) r over k-block
+// kb comes from lane 16 kb + r (sa, sb: the lane's scale in the low byte).
+// FA, FB: element formats, 0 = e4m3, 4 = e2m1.  An e4m3 operand lane l
+// (g = l / 16) holds k 16g..16g+15 in bytes 0..15 and 64+16g..64+16g+15 in
+// bytes 16..31; an e2m1 operand holds k 32g..32g+31 as 32 nibbles (low
+// nibble first) in its first 16 bytes.
+template <int FA, int FB>
+__device__ __forceinline__ f32x4 mfma_mx(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
 // D[16x16] += A[16x32] * B[32x16] in bf16.  Lane l holds row (A) / column
 // (B) l % 16 and the 8 consecutive k at 8 * (l / 16); the result is
 // D[4 * (l / 16) + i][l % 16] in element i.
@@ -61,6 +73,20 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return uint32_t(w);
+}
+
+// MXFP8 shared exponent of a block with maximum magnitude `amax` (OCP MX
+// v1.0): floor(log2 amax) - 8 (8 = the e4m3 emax), at least -127; an
+// all-zero or subnormal amax gives -127.  The E8M0 code is the result + 127.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+  const int ef = int((__float_as_uint(amax) >> 23) & 0xFFu);
+  return max(ef - 127 - 8, -127);
+}
+
+// e4m3 codes of v / 2^X (exact scaling), saturating at 448.
+__device__ __forceinline__ uint32_t mx8x4(float a, float b, float c, float d, int X) {
+  return e4m3x4(__builtin_amdgcn_ldexpf(a, -X), __builtin_amdgcn_ldexpf(b, -X),
+                __builtin_amdgcn_ldexpf(c, -X), __builtin_amdgcn_ldexpf(d, -X));
 }
 
 // Signed int4 -> e4m3 codes, exact.  `nib` holds one nibble value (0..15,

@@ -33,6 +33,8 @@ struct Stage {
   float bs;        // FP8_BLOCK: B row scale of this k-block
   float ws[WT];    // FP8_BLOCK: weight block scale per tile
   f32x4 ws4[WT];   // W4A8: group scales of the lane's 4 rows per tile
+  int bsc;         // MX: the lane's E8M0 B scale (its column, k-block l / 16)
+  int wsc[WT];     // MX: the lane's E8M0 weight scale per tile
 };
 }  // namespace
 
@@ -43,6 +45,9 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
   constexpr int TPW = RG * WT;     // row tiles per workgroup
   constexpr int D = Q == MOE_QUANT_BF16 ? 4 : 2;  // k-steps loaded ahead
   constexpr bool GATED = PHASE == 1 && act_gated(ACT);
+  constexpr bool MX = kMx<Q>;
+  // B bytes of a lane: one 32-byte k-run, or (MX) two 16-byte halves 64 apart
+  constexpr int BRUN = MX ? 16 : T::KSTEP / 4, BHALF = MX ? kMxHalfStride : 16;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rg = wave % RG, kp = wave / RG;
@@ -59,7 +64,7 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
   int brow;
   if (PHASE == 1) brow = f < g.A ? f / g.Kp : 0;
   else brow = m;
-  const uint8_t* bp = g.b + (size_t(brow) * g.K + grp * (T::KSTEP / 4)) * T::EB;
+  const uint8_t* bp = g.b + (size_t(brow) * g.K + grp * BRUN) * T::EB;
   const size_t ebytes = size_t(g.tiles) * g.steps * T::FRAG;
   const uint8_t* wp = g.w + size_t(e) * ebytes + size_t(tile0) * g.steps * T::FRAG + lane * 16;
   const int kblocks = g.K / 128;
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
     }
     const uint8_t* q = bp + size_t(s) * T::KSTEP * T::EB;
 #pragma unroll
-    for (int v = 0; v < T::BV; ++v) S.b[v] = ld16(q + v * 16);
+    for (int v = 0; v < T::BV; ++v) S.b[v] = ld16(q + v * BHALF);
     if (Q == MOE_QUANT_FP8_BLOCK) {
       S.bs = g.b_scale[size_t(brow) * kblocks + s];
 #pragma unroll
@@ -95,12 +100,24 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
         S.ws4[j] = *reinterpret_cast<const f32x4*>(
             g.w_scale + ((size_t(e) * g.tiles + tile0 + j) * g.steps + s) * 16 + grp * 4);
     }
+    if (MX) {
+      S.bsc = g.b_sc8[size_t(brow) * (g.K / 32) + s * 4 + grp];
+#pragma unroll
+      for (int j = 0; j < WT; ++j)
+        S.wsc[j] = g.w_sc8[((size_t(e) * g.tiles + tile0 + j) * g.steps + s) * 64 + lane];
+    }
   };
 
   auto compute = [&](const Stage<Q, WT>& S) {
     if (Q == MOE_QUANT_BF16) {
 #pragma unroll
       for (int j = 0; j < WT; ++j) acc[j] = mfma_bf16(S.a[j][0], S.b[0], acc[j]);
+    } else if (MX) {
+      const i32x8 bb = fp8_pair(S.b[0], S.b[1]);
+#pragma unroll
+      for (int j = 0; j < WT; ++j)
+        acc[j] = mfma_mx<kMxWFmt<Q>, 0>(mx_weight_operand<Q>(S.a[j][0], S.a[j][T::AV - 1]), bb,
+                                        acc[j], S.wsc[j], S.bsc);
     } else {
       const i32x8 bb = fp8_pair(S.b[0], S.b[1]);
 #pragma unroll
@@ -195,6 +212,27 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
           o[0] = bf16_bits(a[v][0]) | (bf16_bits(a[v][1]) << 16);
           o[1] = bf16_bits(a[v][2]) | (bf16_bits(a[v][3]) << 16);
           *reinterpret_cast<u32x2*>(g.out + (size_t(m) * g.I + cbase[v]) * 2) = o;
+        }
+      }
+    } else if (MX) {
+      // MXFP8 per token and 32 channels: vectors 2b and 2b + 1 are block b
+      static_assert(!MX || NV % 2 == 0, "whole 32-channel blocks per wave");
+      if (active) {
+#pragma unroll
+        for (int b = 0; b < NV / 2; ++b) {
+          float am = 0.f;
+#pragma unroll
+          for (int v = 2 * b; v < 2 * b + 2; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(a[v][i]));
+          am = fmaxf(am, __shfl_xor(am, 16, 64));
+          am = fmaxf(am, __shfl_xor(am, 32, 64));
+          const int X = mx8_exponent(am);
+#pragma unroll
+          for (int v = 2 * b; v < 2 * b + 2; ++v)
+            *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) =
+                mx8x4(a[v][0], a[v][1], a[v][2], a[v][3], X);
+          if (grp == 0) g.out_sc8[size_t(m) * (g.I / 32) + cbase[2 * b] / 32] = uint8_t(X + 127);
         }
       }
     } else if (Q == MOE_QUANT_FP8_BLOCK) {
@@ -303,6 +341,10 @@ hipError_t dispatch_stream(const GemmCfg& c, dim3 grid, const GemmArgs& a, hipSt
     // the per-128-channel amax needs the whole workgroup on one row range
     if (c.wt == 4 && c.ksplit == 1) gemm_stream<PHASE, Q, ACT, 4, 1><<<grid, block, 0, st>>>(a);
     else return hipErrorInvalidValue;
+  } else if constexpr (kMx<Q>) {
+    // GEMM1: a wave's 4 tiles hold whole 32-channel scale blocks
+    if (c.wt == 4 && c.ksplit == 4) gemm_stream<PHASE, Q, ACT, 4, 4><<<grid, block, 0, st>>>(a);
+    else return hipErrorInvalidValue;
   } else {
     if (c.wt == 4 && c.ksplit == 1) gemm_stream<PHASE, Q, ACT, 4, 1><<<grid, block, 0, st>>>(a);
     else if (c.wt == 4 && c.ksplit == 2) gemm_stream<PHASE, Q, ACT, 4, 2><<<grid, block, 0, st>>>(a);
@@ -323,6 +365,8 @@ hipError_t dispatch_quant(int quant, const GemmCfg& c, dim3 grid, const GemmArgs
     case MOE_QUANT_FP8_TENSOR: return dispatch_stream<PHASE, MOE_QUANT_FP8_TENSOR, ACT>(c, grid, a, st);
     case MOE_QUANT_FP8_BLOCK: return dispatch_stream<PHASE, MOE_QUANT_FP8_BLOCK, ACT>(c, grid, a, st);
     case MOE_QUANT_W4A8: return dispatch_stream<PHASE, MOE_QUANT_W4A8, ACT>(c, grid, a, st);
+    case MOE_QUANT_MXFP8: return dispatch_stream<PHASE, MOE_QUANT_MXFP8, ACT>(c, grid, a, st);
+    case MOE_QUANT_MXFP4: return dispatch_stream<PHASE, MOE_QUANT_MXFP4, ACT>(c, grid, a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -334,23 +378,26 @@ dim3 stream_grid(const GemmCfg& c, int tiles, int64_t blocks) {
 
 }  // namespace
 
-hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, const float* xs,
+hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, const void* xs,
                         const moe_weights& w, const int32_t* sorted_ids,
                         const int32_t* block_expert, const int32_t* num_padded, void* a2,
-                        float* a2s, hipStream_t stream) {
+                        void* a2s, hipStream_t stream) {
   if (q.max_blocks == 0) return hipSuccess;
   GemmArgs a{};
   a.b = static_cast<const uint8_t*>(x);
-  a.b_scale = xs;
+  a.b_scale = static_cast<const float*>(xs);
+  a.b_sc8 = static_cast<const uint8_t*>(xs);
   a.w = static_cast<const uint8_t*>(w.w13);
-  a.w_scale = w.w13_scale;
+  a.w_scale = static_cast<const float*>(w.w13_scale);
+  a.w_sc8 = static_cast<const uint8_t*>(w.w13_scale);
   a.a1 = w.a1_scale;
   a.a2 = w.a2_scale;
   a.sorted_ids = sorted_ids;
   a.block_expert = block_expert;
   a.num_padded = num_padded;
   a.out = static_cast<uint8_t*>(a2);
-  a.out_scale = a2s;
+  a.out_scale = static_cast<float*>(a2s);
+  a.out_sc8 = static_cast<uint8_t*>(a2s);
   a.K = p.H;
   a.N = q.N1;
   a.I = p.I;
@@ -371,16 +418,18 @@ hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, cons
   return dispatch_quant<1, MOE_ACT_RELU2>(p.quant, q.g1, grid, a, stream);
 }
 
-hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, const float* a2s,
+hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, const void* a2s,
                         const moe_weights& w, const int32_t* sorted_ids,
                         const int32_t* block_expert, const int32_t* num_padded,
                         const float* topk_w, float* y, hipStream_t stream) {
   if (q.max_blocks == 0) return hipSuccess;
   GemmArgs a{};
   a.b = static_cast<const uint8_t*>(a2);
-  a.b_scale = a2s;
+  a.b_scale = static_cast<const float*>(a2s);
+  a.b_sc8 = static_cast<const uint8_t*>(a2s);
   a.w = static_cast<const uint8_t*>(w.w2);
-  a.w_scale = w.w2_scale;
+  a.w_scale = static_cast<const float*>(w.w2_scale);
+  a.w_sc8 = static_cast<const uint8_t*>(w.w2_scale);
   a.a1 = w.a1_scale;
   a.a2 = w.a2_scale;
   a.sorted_ids = sorted_ids;

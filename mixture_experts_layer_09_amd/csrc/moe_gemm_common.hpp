@@ -19,6 +19,9 @@ struct GemmArgs {
   const float* topk_w;       // GEMM2
   uint8_t* out;              // GEMM1: a2 [rows][I]; GEMM2: y fp32 [A][H]
   float* out_scale;          // GEMM1 FP8_BLOCK: [rows][I/128]
+  const uint8_t* b_sc8;      // MX: E8M0 per B row per 32 K
+  const uint8_t* w_sc8;      // MX: packed E8M0 weight scales [E][tiles][steps][64]
+  uint8_t* out_sc8;          // GEMM1 MX: E8M0 [rows][I/32]
   int K, N, I, H, Kp, A, steps, tiles;
   int slices;                // tiled kernel: workgroups along the weight rows
   int nwg;                   // tiled kernel: real workgroups (grid is padded to 8)
@@ -39,6 +42,36 @@ template <> struct QT<MOE_QUANT_FP8_BLOCK> {
 template <> struct QT<MOE_QUANT_W4A8> {
   static constexpr int AV = 1, BV = 2, FRAG = 1024, KSTEP = 128, EB = 1;
 };
+template <> struct QT<MOE_QUANT_MXFP8> {
+  static constexpr int AV = 2, BV = 2, FRAG = 2048, KSTEP = 128, EB = 1;
+};
+template <> struct QT<MOE_QUANT_MXFP4> {
+  static constexpr int AV = 1, BV = 2, FRAG = 1024, KSTEP = 128, EB = 1;
+};
+
+template <int Q> constexpr bool kMx = Q == MOE_QUANT_MXFP8 || Q == MOE_QUANT_MXFP4;
+// Element format of the weights in the scaled MFMA: 0 e4m3, 4 e2m1.
+template <int Q> constexpr int kMxWFmt = Q == MOE_QUANT_MXFP4 ? 4 : 0;
+
+// An MX token (B) fragment's two 16-byte halves: k 16g.. and 64+16g.. of the
+// k-step for lane group g (the scaled MFMA's e4m3 operand order).
+constexpr int kMxHalfStride = 64;
+
+// The weight operand of the scaled MFMA from a fragment's lane bytes.
+template <int Q>
+__device__ __forceinline__ i32x8 mx_weight_operand(const u32x4& lo, const u32x4& hi) {
+  if constexpr (Q == MOE_QUANT_MXFP4) {
+    i32x8 r;
+    r[0] = int(lo[0]); r[1] = int(lo[1]); r[2] = int(lo[2]); r[3] = int(lo[3]);
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+  } else {
+    i32x8 r;
+    r[0] = int(lo[0]); r[1] = int(lo[1]); r[2] = int(lo[2]); r[3] = int(lo[3]);
+    r[4] = int(hi[0]); r[5] = int(hi[1]); r[6] = int(hi[2]); r[7] = int(hi[3]);
+    return r;
+  }
+}
 
 __device__ __forceinline__ i32x8 fp8_pair(const u32x4& lo, const u32x4& hi) {
   i32x8 r;

@@ -237,7 +237,13 @@ template <int Q, int WC, int NWV, int WT = 4, int NW = 8> struct LdsCfg {
   static constexpr int TILES = WT * WR, NT = NW * WC;  // weight / token tiles per workgroup
   static constexpr int A_BYTES = TILES * QT<Q>::FRAG;
   static constexpr int B_BYTES = NT * 2048;
-  static constexpr int SC_BYTES = (Q == MOE_QUANT_FP8_BLOCK || Q == MOE_QUANT_W4A8) ? 1024 : 0;
+  // scales of a stage: fp8 block / int4 group scales in 1 KiB; MX: E8M0
+  // weight scales (64 bytes per tile) then the token rows' (4 bytes per row,
+  // and as much again for the waves whose copies are not read)
+  static constexpr int SC_W8 = kMx<Q> ? TILES * 64 : 0;
+  static constexpr int SC_BYTES = (Q == MOE_QUANT_FP8_BLOCK || Q == MOE_QUANT_W4A8) ? 1024
+                                  : kMx<Q> ? SC_W8 + NWV * 256 : 0;
+  static constexpr int SC_LOADS = kMx<Q> ? SC_W8 / (NWV * 256) + 1 : (SC_BYTES ? 1 : 0);
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   // stages: as many as fit, at most 4
 #ifdef MOE_LDS_MAX_STAGES
@@ -247,11 +253,13 @@ template <int Q, int WC, int NWV, int WT = 4, int NW = 8> struct LdsCfg {
 #endif
   static constexpr int S = (160 * 1024 - 4096) / STAGE < SMAX ? (160 * 1024 - 4096) / STAGE : SMAX;
   // loads per wave per stage: weight fragments, token fragments, scales
-  static constexpr int LOADS = TILES * QT<Q>::AV / NWV + NT * 2 / NWV + (SC_BYTES ? 1 : 0);
+  static constexpr int LOADS = TILES * QT<Q>::AV / NWV + NT * 2 / NWV + SC_LOADS;
   static_assert(S * STAGE <= 160 * 1024 - 4096, "stage buffers exceed the LDS");
   static_assert(Q != MOE_QUANT_FP8_BLOCK || WC == 1,
                 "block scales: one workgroup spans the 128 output channels of a group");
   static_assert(TILES % NWV == 0 && NT % NWV == 0, "whole fragments per wave");
+  static_assert(!kMx<Q> || (SC_W8 % (NWV * 256) == 0 && NT * 16 <= 128 && NWV >= 2),
+                "MX: whole 256-byte weight-scale loads per wave, token rows in two waves");
 };
 
 // GEMM1 epilogue of the 8-wave fp8 per-tensor tile through the LDS: each
@@ -356,6 +364,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
     const bool active = tile0 < g.tiles && ct > 0;
     const int kblocks = g.K / 128;
     const int nst = g.K / 128;
+    constexpr bool MX = kMx<Q>;
+    constexpr int BRUN = MX ? 16 : 32, BHALF = MX ? kMxHalfStride : 16;
 
     // ---- per-lane source addresses, fixed over the stages
     const size_t ebytes = size_t(g.tiles) * g.steps * T::FRAG;
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       } else {
         brow = row0 + r;
       }
-      bsrc[q] = uint32_t(brow) * uint32_t(g.K) + grp * 32;
+      bsrc[q] = uint32_t(brow) * uint32_t(g.K) + grp * BRUN;
     }
     // scales of a stage: fp8-block token-row scales (waves 1, 2) and weight
     // scales (every other wave, the same values); W4A8 group scales (every
@@ -411,6 +421,28 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       const int t = min(wg_tile0 + lane / 4, g.tiles - 1);
       ssrc = g.w_scale + (size_t(e) * g.tiles + t) * g.steps * 16 + (lane % 4) * 4;
     }
+    // MX: the weight scales of tiles 4 (j NWV + wave) .. +3, 4 bytes per lane
+    // (lane l: tile + l / 16, bytes 4 (l % 16) of the tile's 64); the token
+    // row scales (4 k-blocks, 4 bytes) of row 64 (wave % 2) + lane
+    constexpr int MXW = C::SC_LOADS - 1;  // weight-scale loads per wave
+    const uint8_t* mx_wsrc[MXW > 0 ? MXW : 1];
+    const uint8_t* mx_tsrc = nullptr;
+    if constexpr (MX) {
+#pragma unroll
+      for (int j = 0; j < MXW; ++j) {
+        const int t = min(wg_tile0 + 4 * (j * NWV + wave) + lane / 16, g.tiles - 1);
+        mx_wsrc[j] = g.w_sc8 + (size_t(e) * g.tiles + t) * g.steps * 64 + (lane % 16) * 4;
+      }
+      const int r = 64 * (wave % 2) + lane;
+      int brow;
+      if (PHASE == 1) {
+        const int f = r < BM ? g.sorted_ids[row0 + r] : g.A;
+        brow = f < g.A ? f / g.Kp : 0;
+      } else {
+        brow = r < BM ? row0 + r : row0;
+      }
+      mx_tsrc = g.b_sc8 + size_t(brow) * (g.K / 32);
+    }
 
     auto issue = [&](auto bufc, int st) {
       uint8_t* base = stage_buf(bufc);
@@ -424,10 +456,17 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       for (int q = 0; q < LB; ++q)
   #pragma unroll
         for (int h = 0; h < 2; ++h)
-          ld_lds16(g.b + bsrc[q] + size_t(st) * 128 + h * 16,
+          ld_lds16(g.b + bsrc[q] + size_t(st) * 128 + h * BHALF,
                      base + C::A_BYTES + (LB * wave + q) * 2048 + h * 1024);
       if (Q == MOE_QUANT_FP8_BLOCK) ld_lds4(ssrc + st, base + C::A_BYTES + C::B_BYTES + sdst);
       if (Q == MOE_QUANT_W4A8) ld_lds16(ssrc + size_t(st) * 16, base + C::A_BYTES + C::B_BYTES);
+      if constexpr (MX) {
+  #pragma unroll
+        for (int j = 0; j < MXW; ++j)
+          ld_lds4(mx_wsrc[j] + size_t(st) * 64,
+                  base + C::A_BYTES + C::B_BYTES + (j * NWV + wave) * 256);
+        ld_lds4(mx_tsrc + st * 4, base + C::A_BYTES + C::B_BYTES + C::SC_W8 + wave * 256);
+      }
     };
 
     f32x4 acc[WT][NW];
@@ -451,7 +490,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       i32x8 a8[WT];
   #pragma unroll
       for (int r = 0; r < WT; ++r) {
-        if (Q == MOE_QUANT_W4A8) {
+        if constexpr (MX) {
+          a8[r] = mx_weight_operand<Q>(rd16(base, a_off + r * T::FRAG),
+                                       rd16(base, a_off + r * T::FRAG + (T::AV - 1) * 1024));
+        } else if (Q == MOE_QUANT_W4A8) {
           a8[r] = int4x32_to_e4m3(rd16(base, a_off + r * T::FRAG));
         } else {
           a8[r] = fp8_pair(rd16(base, a_off + r * T::FRAG), rd16(base, a_off + r * T::FRAG + 1024));
@@ -459,6 +501,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       }
       float ws[WT];
       f32x4 ws4[WT];
+      int wsc[WT];
+      if constexpr (MX) {
+        const int so = C::A_BYTES + C::B_BYTES + wr * WT * 64 + lane;
+  #pragma unroll
+        for (int r = 0; r < WT; ++r) wsc[r] = base[so + r * 64];
+      }
       if (Q == MOE_QUANT_FP8_BLOCK) {
   #pragma unroll
         for (int r = 0; r < WT; ++r) ws[r] = sc[wr * WT + r];
@@ -472,7 +520,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       for (int c = 0; c < NW; ++c) {
         if (c < ct) {
           const i32x8 bb = fp8_pair(rd16(base, b_off + c * 2048), rd16(base, b_off + c * 2048 + 1024));
-          if (Q == MOE_QUANT_FP8_TENSOR) {
+          if constexpr (MX) {
+            // token row c*16 + lrow of this wave's group, k-block grp of the step
+            const int bsc = base[C::A_BYTES + C::B_BYTES + C::SC_W8 +
+                                 ((wc * NW + c) * 16 + lrow) * 4 + grp];
+  #pragma unroll
+            for (int r = 0; r < WT; ++r)
+              acc[r][c] = mfma_mx<kMxWFmt<Q>, 0>(a8[r], bb, acc[r][c], wsc[r], bsc);
+          } else if (Q == MOE_QUANT_FP8_TENSOR) {
   #pragma unroll
             for (int r = 0; r < WT; ++r) acc[r][c] = mfma_fp8(a8[r], bb, acc[r][c]);
           } else {
@@ -624,10 +679,14 @@ hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
       return hipErrorInvalidValue;
     }
   }
-  if (c.nt == 8) gemm_tiled<PHASE, Q, ACT, 4, 8><<<grid, block, 0, st>>>(a);
-  else if (c.nt == 4) gemm_tiled<PHASE, Q, ACT, 4, 4><<<grid, block, 0, st>>>(a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if constexpr (kMx<Q>) {
+    return hipErrorInvalidValue;  // MX prefill runs the LDS pipeline only
+  } else {
+    if (c.nt == 8) gemm_tiled<PHASE, Q, ACT, 4, 8><<<grid, block, 0, st>>>(a);
+    else if (c.nt == 4) gemm_tiled<PHASE, Q, ACT, 4, 4><<<grid, block, 0, st>>>(a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
 }
 
 }  // namespace
@@ -640,6 +699,8 @@ hipError_t launch_gemm_tiled(int phase, const moe_problem& p, const GemmCfg& c,
     case MOE_QUANT_FP8_TENSOR: return dispatch_tiled<PH, MOE_QUANT_FP8_TENSOR, ACT>(c, a, st); \
     case MOE_QUANT_FP8_BLOCK: return dispatch_tiled<PH, MOE_QUANT_FP8_BLOCK, ACT>(c, a, st); \
     case MOE_QUANT_W4A8: return dispatch_tiled<PH, MOE_QUANT_W4A8, ACT>(c, a, st);           \
+    case MOE_QUANT_MXFP8: return dispatch_tiled<PH, MOE_QUANT_MXFP8, ACT>(c, a, st);         \
+    case MOE_QUANT_MXFP4: return dispatch_tiled<PH, MOE_QUANT_MXFP4, ACT>(c, a, st);         \
   }
   if (phase == 1) {
     switch (p.act) {

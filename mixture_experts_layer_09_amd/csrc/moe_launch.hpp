@@ -27,23 +27,23 @@ bool prologue_fits(const moe_problem& p, const Plan& q);
 // decode-sized batches, the separate kernels otherwise.
 hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* logits,
                            int32_t* ids, float* w, const uint16_t* x, const float* a1,
-                           uint8_t* xq, float* xs, bool quantise, int32_t* sorted_ids,
+                           uint8_t* xq, void* xs, bool quantise, int32_t* sorted_ids,
                            int32_t* block_expert, int32_t* offsets, int32_t* num_padded,
                            int32_t* scratch, hipStream_t stream);
 
 hipError_t launch_quant_act(const moe_problem& p, const uint16_t* x, const float* a1,
-                            uint8_t* xq, float* xs, hipStream_t stream);
+                            uint8_t* xq, void* xs, hipStream_t stream);
 
 hipError_t launch_pack_w(const moe_problem& p, const Plan& q, int which, const void* src,
                          int32_t src_I, int32_t swap, const void* src_scale, void* dst,
                          void* dst_scale, hipStream_t stream);
 
-hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, const float* xs,
+hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, const void* xs,
                         const moe_weights& w, const int32_t* sorted_ids,
                         const int32_t* block_expert, const int32_t* num_padded, void* a2,
-                        float* a2s, hipStream_t stream);
+                        void* a2s, hipStream_t stream);
 
-hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, const float* a2s,
+hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, const void* a2s,
                         const moe_weights& w, const int32_t* sorted_ids,
                         const int32_t* block_expert, const int32_t* num_padded,
                         const float* topk_w, float* y, hipStream_t stream);

@@ -17,10 +17,17 @@
 //      bf16 : 1 KiB fragments, 16 B per lane;
 //      fp8  : 2 KiB fragments, lane bytes 0..15 at l*16, 16..31 at 1024 + l*16;
 //      int4 : 1 KiB fragments, 16 B per lane; byte b of lane dword q holds
-//             k-run element 8q+b in its low nibble and 8q+4+b in its high one.
+//             k-run element 8q+b in its low nibble and 8q+4+b in its high one;
+//      MXFP8: 2 KiB fragments in the scaled MFMA's e4m3 order: lane l
+//             (g = l/16) holds k 16g..16g+15 at l*16 and 64+16g..64+16g+15 at
+//             1024 + l*16;
+//      MXFP4: 1 KiB fragments, lane l holds k 32g..32g+31 as 32 nibbles, the
+//             even k in the low nibble (the checkpoint's own nibble order);
 //  * block scales (fp8 128x128) keep the checkpoint's row order (the halves
 //    swapped when asked); int4 group scales become fp32 in packed row order,
-//    [E][tiles][steps][16].
+//    [E][tiles][steps][16]; MX E8M0 scales one byte per fragment lane,
+//    [E][tiles][steps][64], lane l holding the scale of row t*16 + l%16 over
+//    k-block 4s + l/16 (the lane that feeds it to the scaled MFMA).
 #include "moe_device.hpp"
 #include "moe_launch.hpp"
 
@@ -50,25 +57,26 @@ __device__ __forceinline__ int w13_src_row(const PackArgs& a, int r) {
 }
 
 // Element `k` of checkpoint row `sr` of expert e as raw bits (bf16: 16 bits,
-// fp8: 8 bits, int4: the 4-bit nibble), or 0 outside the checkpoint.
+// fp8: 8 bits, int4 / fp4: the 4-bit nibble), or 0 outside the checkpoint.
 template <int FMT>
 __device__ __forceinline__ uint32_t src_elem(const PackArgs& a, int e, int sr, int k) {
   if (sr < 0 || k >= a.src_K) return 0;  // zero padding rows / columns
   const size_t idx = (size_t(e) * a.src_rows + sr) * a.src_K + k;
   if (FMT == 0) return reinterpret_cast<const uint16_t*>(a.src)[idx];
-  if (FMT == 1) return a.src[idx];
+  if (FMT == 1 || FMT == 3) return a.src[idx];
   const uint8_t b = a.src[idx / 2];
   return (idx & 1) ? (b >> 4) : (b & 0xF);
 }
 
 }  // namespace
 
-// One thread per 16 bytes of packed output.  FMT: 0 bf16, 1 fp8, 2 int4.
+// One thread per 16 bytes of packed output.  FMT: 0 bf16, 1 fp8, 2 int4,
+// 3 MXFP8, 4 MXFP4.
 template <int FMT>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int64_t n16) {
   const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (c >= n16) return;
-  constexpr int frag_chunks = FMT == 1 ? 128 : 64;  // 16-B chunks per fragment
+  constexpr int frag_chunks = (FMT == 1 || FMT == 3) ? 128 : 64;  // 16-B chunks per fragment
   const int64_t frag = c / frag_chunks;
   const int cf = int(c % frag_chunks);
   const int lane = cf % 64, half = cf / 64;
@@ -85,11 +93,17 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int64_t n16) {
     for (int j = 0; j < 8; ++j) {
       out[j / 2] |= src_elem<0>(a, e, sr, k0 + j) << (16 * (j & 1));
     }
-  } else if (FMT == 1) {
-    const int k0 = s * 128 + g * 32 + half * 16;
+  } else if (FMT == 1 || FMT == 3) {
+    const int k0 = FMT == 1 ? s * 128 + g * 32 + half * 16 : s * 128 + half * 64 + g * 16;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      out[j / 4] |= src_elem<1>(a, e, sr, k0 + j) << (8 * (j & 3));
+      out[j / 4] |= src_elem<FMT>(a, e, sr, k0 + j) << (8 * (j & 3));
+    }
+  } else if (FMT == 4) {
+    const int k0 = s * 128 + g * 32;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      out[j / 8] |= src_elem<4>(a, e, sr, k0 + j) << (4 * (j & 7));
     }
   } else {
     const int k0 = s * 128 + g * 32;
@@ -143,6 +157,26 @@ __global__ void pack_group_scales(PackArgs a, const uint16_t* __restrict__ src,
   dst[i] = v;
 }
 
+// MX E8M0 scales (bytes [E][src_rows][src_K/32]) -> [E][tiles][steps][64]:
+// byte l of fragment (t, s) is the scale of packed row t*16 + l%16 over
+// k-block 4s + l/16.  Padding rows and columns take 127 (2^0; their weights
+// are zero).
+__global__ void pack_mx_scales(PackArgs a, const uint8_t* __restrict__ src,
+                               uint8_t* __restrict__ dst, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int l = int(i % 64);
+  const int s = int((i / 64) % a.steps);
+  const int64_t et = i / (64 * int64_t(a.steps));
+  const int tiles = a.rows / 16;
+  const int t = int(et % tiles), e = int(et / tiles);
+  const int r = t * 16 + l % 16, kb = 4 * s + l / 16;
+  const int sr = a.which == 13 ? w13_src_row(a, r) : r;
+  uint8_t v = 127;
+  if (sr >= 0 && kb * 32 < a.src_K) v = src[(size_t(e) * a.src_rows + sr) * (a.src_K / 32) + kb];
+  dst[i] = v;
+}
+
 hipError_t launch_pack_w(const moe_problem& p, const Plan& q, int which, const void* src,
                          int32_t src_I, int32_t swap, const void* src_scale, void* dst,
                          void* dst_scale, hipStream_t stream) {
@@ -173,6 +207,8 @@ hipError_t launch_pack_w(const moe_problem& p, const Plan& q, int which, const v
   const dim3 grid(unsigned((n16 + 255) / 256)), block(256);
   if (p.quant == MOE_QUANT_BF16) pack_kernel<0><<<grid, block, 0, stream>>>(a, n16);
   else if (p.quant == MOE_QUANT_W4A8) pack_kernel<2><<<grid, block, 0, stream>>>(a, n16);
+  else if (p.quant == MOE_QUANT_MXFP8) pack_kernel<3><<<grid, block, 0, stream>>>(a, n16);
+  else if (p.quant == MOE_QUANT_MXFP4) pack_kernel<4><<<grid, block, 0, stream>>>(a, n16);
   else pack_kernel<1><<<grid, block, 0, stream>>>(a, n16);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -186,6 +222,12 @@ hipError_t launch_pack_w(const moe_problem& p, const Plan& q, int which, const v
     pack_block_scales<<<unsigned((n + 255) / 256), 256, 0, stream>>>(
         static_cast<const float*>(src_scale), static_cast<float*>(dst_scale), p.E, rb, kb,
         which == 13 && q.gated && swap ? 1 : 0);
+    return hipGetLastError();
+  }
+  if (quant_is_mx(p.quant)) {
+    const int64_t n = int64_t(p.E) * (a.rows / 16) * a.steps * 64;
+    pack_mx_scales<<<unsigned((n + 255) / 256), 256, 0, stream>>>(
+        a, static_cast<const uint8_t*>(src_scale), static_cast<uint8_t*>(dst_scale), n);
     return hipGetLastError();
   }
   if (p.quant == MOE_QUANT_W4A8) {

@@ -61,7 +61,7 @@ bool is_gated(int32_t act) { return act != MOE_ACT_RELU2; }
 
 int32_t padded_intermediate(int32_t I, int32_t act, int32_t quant) {
   if (!valid_act(act)) return MOE_ERR_INVALID_ARG;
-  if (quant < MOE_QUANT_BF16 || quant > MOE_QUANT_W4A8) return MOE_ERR_INVALID_ARG;
+  if (quant < MOE_QUANT_BF16 || quant > MOE_QUANT_MXFP4) return MOE_ERR_INVALID_ARG;
   if (I <= 0) return MOE_ERR_INVALID_ARG;
   // the TRTLLM-Gen rule: 16 for gated, 128 for the non-gated relu2 path
   int32_t a = is_gated(act) ? 16 : 128;
@@ -81,7 +81,9 @@ size_t packed_weight_bytes(const moe_problem& p, int which) {
     case MOE_QUANT_BF16: return size_t(elems) * 2;
     case MOE_QUANT_FP8_TENSOR:
     case MOE_QUANT_FP8_BLOCK: return size_t(elems);
-    case MOE_QUANT_W4A8: return size_t(elems / 2);
+    case MOE_QUANT_W4A8:
+    case MOE_QUANT_MXFP4: return size_t(elems / 2);
+    case MOE_QUANT_MXFP8: return size_t(elems);
   }
   return 0;
 }
@@ -95,6 +97,8 @@ size_t packed_scale_bytes(const moe_problem& p, int which) {
     case MOE_QUANT_FP8_TENSOR: return size_t(p.E) * 4;
     case MOE_QUANT_FP8_BLOCK: return size_t(p.E) * (n / kGroup) * (k / kGroup) * 4;
     case MOE_QUANT_W4A8: return size_t(p.E) * n * (k / kGroup) * 4;
+    case MOE_QUANT_MXFP8:
+    case MOE_QUANT_MXFP4: return size_t(p.E) * n * (k / kMxBlock);  // one E8M0 byte each
   }
   return 0;
 }
@@ -105,7 +109,7 @@ int make_plan(const moe_problem* p, Plan* plan) {
   if (!valid_act(p->act))
     return fail(MOE_ERR_INVALID_ARG,
                 "act must be MOE_ACT_SILU_GATED, MOE_ACT_RELU2 or MOE_ACT_GELU_TANH_GATED");
-  if (p->quant < MOE_QUANT_BF16 || p->quant > MOE_QUANT_W4A8)
+  if (p->quant < MOE_QUANT_BF16 || p->quant > MOE_QUANT_MXFP4)
     return fail(MOE_ERR_INVALID_ARG, "unknown quant mode");
   if (p->T < 0 || p->H <= 0 || p->I <= 0)
     return fail(MOE_ERR_INVALID_ARG, "T must be >= 0, H and I > 0");
@@ -165,6 +169,8 @@ int make_plan(const moe_problem* p, Plan* plan) {
   if (q.BM == 256 && !wide_ok)
     return fail(MOE_ERR_UNSUPPORTED,
                 "block_m = 256 runs for the fp8 per-tensor and int4 (W4A8) modes only");
+  if (quant_is_mx(p->quant) && q.BM != 16 && q.BM != 128)
+    return fail(MOE_ERR_UNSUPPORTED, "the MX modes run block_m = 16 and 128");
   const int64_t nz = std::min<int64_t>(p->E, q.A);
   q.max_blocks = std::min<int64_t>(q.A, (q.A + nz * (q.BM - 1)) / q.BM);
   q.max_rows = q.max_blocks * q.BM;
@@ -180,6 +186,8 @@ int make_plan(const moe_problem* p, Plan* plan) {
   q.a2_elem = p->quant == MOE_QUANT_BF16 ? 2 : 1;
   if (q.BM == 16) {
     q.g1 = stream_shape(1, p->quant == MOE_QUANT_FP8_BLOCK);
+    // MX: a workgroup's 64 interleaved rows are whole 32-channel scale blocks
+    if (quant_is_mx(p->quant)) q.g1 = kStreamShapes[2];
     q.g2 = stream_shape(2, false);
   } else {
     // fp8 / int4 weights at 128-row blocks: weights and tokens staged in LDS by
@@ -210,9 +218,14 @@ int make_plan(const moe_problem* p, Plan* plan) {
   q.off_align = take(q.align_ws);
   const bool fp8_act = quant_is_fp8_act(p->quant);
   q.off_xq = take(fp8_act ? size_t(p->T) * p->H : 0);
-  q.off_xs = take(p->quant == MOE_QUANT_FP8_BLOCK ? size_t(p->T) * (p->H / kGroup) * 4 : 0);
+  const bool mx = quant_is_mx(p->quant);
+  q.off_xs = take(p->quant == MOE_QUANT_FP8_BLOCK ? size_t(p->T) * (p->H / kGroup) * 4
+                  : mx                            ? size_t(p->T) * (p->H / kMxBlock)
+                                                  : 0);
   q.off_a2 = take(size_t(q.max_rows) * p->I * q.a2_elem);
-  q.off_a2s = take(p->quant == MOE_QUANT_FP8_BLOCK ? size_t(q.max_rows) * (p->I / kGroup) * 4 : 0);
+  q.off_a2s = take(p->quant == MOE_QUANT_FP8_BLOCK ? size_t(q.max_rows) * (p->I / kGroup) * 4
+                   : mx                            ? size_t(q.max_rows) * (p->I / kMxBlock)
+                                                   : 0);
   q.off_y = take(q.combine_ws);
   q.ws_total = o;
   *plan = q;

@@ -16,6 +16,10 @@ constexpr int kAlignChunk = 1024;  // assignments per workgroup in the align ker
 constexpr int kMaxRouted = 1024;   // logits per token the routing kernel holds
 constexpr int kMaxSlots = 64;      // K' = top_k + n_shared limit (one lane each)
 constexpr int kTiledMinRows = 48;  // rows per expert from which the tiled GEMMs run
+constexpr int kMxBlock = 32;       // elements per E8M0 scale in the MX modes
+
+// The OCP MX modes (E8M0 scales per 32 K on weights and activations).
+inline bool quant_is_mx(int q) { return q == MOE_QUANT_MXFP8 || q == MOE_QUANT_MXFP4; }
 
 // Which GEMM kernel runs and how it is tiled.
 //  kind 0: weight-streaming kernel, one 16-row block of tokens per workgroup,

@@ -43,7 +43,37 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
           }
         }
     };
-    if (Q == MOE_QUANT_FP8_BLOCK) {
+    if constexpr (kMx<Q>) {
+      // MXFP8 per token and 32 channels: vectors 2b and 2b + 1 are block b
+      static_assert(NV % 2 == 0, "whole 32-channel blocks per wave");
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          if (c < ct) {
+            float a[NV][4];
+            act(c, a);
+            const int m = row0 + c * 16 + mylane_row;
+#pragma unroll
+            for (int b = 0; b < NV / 2; ++b) {
+              float am = 0.f;
+#pragma unroll
+              for (int v = 2 * b; v < 2 * b + 2; ++v)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(a[v][i]));
+              am = fmaxf(am, __shfl_xor(am, 16, 64));
+              am = fmaxf(am, __shfl_xor(am, 32, 64));
+              const int X = mx8_exponent(am);
+#pragma unroll
+              for (int v = 2 * b; v < 2 * b + 2; ++v)
+                *reinterpret_cast<uint32_t*>(g.out + size_t(m) * g.I + cbase[v]) =
+                    mx8x4(a[v][0], a[v][1], a[v][2], a[v][3], X);
+              if (grp == 0)
+                g.out_sc8[size_t(m) * (g.I / 32) + cbase[2 * b] / 32] = uint8_t(X + 127);
+            }
+          }
+        }
+      }
+    } else if (Q == MOE_QUANT_FP8_BLOCK) {
       // per token and 128 channels: s = amax / 448, q = e4m3(a / s)
       constexpr int CH = NV * 16;    // channels per wave
       constexpr int WPG = 128 / CH;  // waves per 128-channel group

@@ -18,8 +18,9 @@ class MoELayer:
     """Packed weights of one MoE layer plus the per-call plumbing.
 
     w13, w2: checkpoint layout on the device (uint16 bf16 bits, uint8 e4m3
-    codes, or uint8 packed int4); scales as the header describes; a1, a2:
-    0-d float32 device tensors for the per-tensor modes.
+    codes, or uint8 packed int4 / fp4); scales as the header describes (uint8
+    E8M0 for the MX modes); a1, a2: 0-d float32 device tensors for the
+    per-tensor modes.
     """
 
     def __init__(self, H, I, E_routed, top_k, act, quant, w13, w2, w13_scale=None,
@@ -35,8 +36,8 @@ class MoELayer:
         b2, s2 = packed_bytes(p, 2)
         self.w13 = _bytes(b13, dev)
         self.w2 = _bytes(b2, dev)
-        self.s13 = torch.empty(max(s13 // 4, 1), dtype=torch.float32, device=dev)
-        self.s2 = torch.empty(max(s2 // 4, 1), dtype=torch.float32, device=dev)
+        self.s13 = _bytes(s13, dev)
+        self.s2 = _bytes(s2, dev)
         src_I = I if src_I is None else src_I
         moe_pack_w13(p, w13, src_I, swap_halves, w13_scale, self.w13, self.s13)
         moe_pack_w2(p, w2, src_I, w2_scale, self.w2, self.s2)
@@ -80,11 +81,14 @@ class MoELayer:
             align_ws=_bytes(align_workspace_bytes(p), dev),
             xq=None if q == "bf16" else torch.empty((T, H), dtype=torch.uint8, device=dev),
             xs=torch.empty((T, H // 128), dtype=torch.float32, device=dev)
-            if q == "fp8_block" else None,
+            if q == "fp8_block" else
+            torch.empty((T, H // 32), dtype=torch.uint8, device=dev) if q.startswith("mx") else None,
             a2=torch.empty((max(rows, 1), I), dtype=torch.bfloat16 if q == "bf16" else torch.uint8,
                            device=dev),
             a2s=torch.empty((max(rows, 1), I // 128), dtype=torch.float32, device=dev)
-            if q == "fp8_block" else None,
+            if q == "fp8_block" else
+            torch.empty((max(rows, 1), I // 32), dtype=torch.uint8, device=dev)
+            if q.startswith("mx") else None,
             y=_bytes(combine_workspace_bytes(p), dev),
             out=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
         )

@@ -16,6 +16,7 @@ from synth.configs import MoEConfig
 from synth.inputs import bf16_bits_to_f32
 
 TOL = {"bf16": (2e-2, 1e-2), "fp8_tensor": (2e-2, 1e-2), "fp8_block": (2e-2, 1e-2),
+       "mxfp8": (2e-2, 1e-2), "mxfp4": (2e-2, 1e-2),
        "w4a8": (None, 3e-2)}
 
 
@@ -46,10 +47,11 @@ _weights_cache = {}
 
 def weights_for(cfg: MoEConfig):
     """Host weights of a configuration (one configuration kept at a time)."""
-    if cfg.name not in _weights_cache:
+    key = (cfg.name, cfg.quant, cfg.N1)
+    if key not in _weights_cache:
         _weights_cache.clear()
-        _weights_cache[cfg.name] = synth.make_weights(cfg)
-    return _weights_cache[cfg.name]
+        _weights_cache[key] = synth.make_weights(cfg)
+    return _weights_cache[key]
 
 
 def build_layer(cfg: MoEConfig, W, a1=None, a2=None, **kw):

@@ -49,7 +49,7 @@ def _st(lib, p):
 
 
 def test_valid_problems(plan):
-    for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8"):
+    for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8", "mxfp8", "mxfp4"):
         for a in ("silu", "relu2", "gelu_tanh"):
             assert _st(plan, P(quant=q, act=a)) == moe.MOE_OK
     assert _st(plan, P(T=0)) == moe.MOE_OK
@@ -66,6 +66,10 @@ def test_valid_problems(plan):
     (dict(act=3), moe.MOE_ERR_INVALID_ARG),
     (dict(act=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(quant=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(quant=6), moe.MOE_ERR_INVALID_ARG),
+    (dict(quant="mxfp8", block_m=64), moe.MOE_ERR_UNSUPPORTED),   # MX: 16 or 128
+    (dict(quant="mxfp4", block_m=256), moe.MOE_ERR_UNSUPPORTED),
+    (dict(quant="mxfp4", I=160), moe.MOE_ERR_ALIGNMENT),          # MX needs 128
     (dict(block_m=17), moe.MOE_ERR_INVALID_ARG),
     (dict(block_m=256), moe.MOE_ERR_UNSUPPORTED),                 # 256: fp8 per-tensor, W4A8
     (dict(H=200), moe.MOE_ERR_ALIGNMENT),
@@ -100,6 +104,7 @@ def test_padded_intermediate(plan):
     assert f(768, 0, 0) == 768 and f(1000, 0, 0) == 1024 and f(17, 0, 0) == 32
     assert f(2688, 1, 1) == 2688 and f(2600, 1, 0) == 2688 and f(100, 0, 2) == 128
     assert f(1000, 2, 0) == 1024 and f(17, 2, 0) == 32 and f(100, 2, 2) == 128  # gelu_tanh: gated
+    assert f(100, 0, 4) == 128 and f(200, 1, 5) == 256 and f(6, 0, 6) == moe.MOE_ERR_INVALID_ARG
     assert f(0, 0, 0) == moe.MOE_ERR_INVALID_ARG and f(10, 3, 0) == moe.MOE_ERR_INVALID_ARG
 
 
@@ -123,7 +128,9 @@ def test_packed_bytes(plan):
     cases = [("bf16", "silu", 8 * 1024 * 256 * 2, 0), ("fp8_tensor", "relu2", 8 * 512 * 256, 32),
              ("bf16", "gelu_tanh", 8 * 1024 * 256 * 2, 0),
              ("fp8_block", "silu", 8 * 1024 * 256, 8 * 8 * 2 * 4),
-             ("w4a8", "silu", 8 * 1024 * 256 // 2, 8 * 1024 * 2 * 4)]
+             ("w4a8", "silu", 8 * 1024 * 256 // 2, 8 * 1024 * 2 * 4),
+             ("mxfp8", "silu", 8 * 1024 * 256, 8 * 1024 * 256 // 32),      # one E8M0 per 32
+             ("mxfp4", "relu2", 8 * 512 * 256 // 2, 8 * 512 * 256 // 32)]
     for q, a, wb, sb in cases:
         p = P(quant=q, act=a)
         assert plan.moe_packed_bytes(ctypes.byref(p), 13, ctypes.byref(w), ctypes.byref(s)) == 0

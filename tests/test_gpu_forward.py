@@ -78,7 +78,34 @@ def test_forward_gelu_tanh_full_size(cid, M, n):
     torch.cuda.empty_cache()
 
 
-SMALL = [(q, a) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
+# The MX modes at full size: the decode shape (hidden 2048, 128 experts,
+# top-8, intermediate 768) and the fp8 block-scale prefill shape (hidden
+# 2048, 512 + 1 experts, top-10, intermediate 512), with MXFP8 and MXFP4
+# weights in place of the configuration's own.
+MX_FULL = [(2, 64, None, q) for q in ("mxfp8", "mxfp4")] + \
+          [(3, 4096, 10, q) for q in ("mxfp8", "mxfp4")] + [(5, 8192, 6, "mxfp4")]
+
+
+@pytest.mark.parametrize("cid,M,n,quant", MX_FULL,
+                         ids=[f"cfg{c}-M{m}-{q}" for c, m, _, q in MX_FULL])
+def test_forward_mx_full_size(cid, M, n, quant):
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS[cid], quant=quant)
+    say(f"forward {quant} {cfg.name} M={M} sample={n}")
+    W = weights_for(cfg)
+    tok = synth.make_tokens(cfg, M)
+    layer = build_layer(cfg, W)
+    out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    rows = _sample(M, n, 9000 * cid + M)
+    ref = oracle_forward(cfg, W, tok["x_bits"][rows], tok["logits"][rows])
+    assert_close(got[rows], ref, quant, f"{quant} {cfg.name} M={M}")
+    del layer
+    torch.cuda.empty_cache()
+
+
+SMALL = [(q, a) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8", "mxfp8", "mxfp4")
          for a in ("silu", "relu2", "gelu_tanh")]
 
 
@@ -207,7 +234,8 @@ def test_invalid_call_enqueues_nothing():
 
 TILED = [(q, a, bm) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
          for a in ("silu", "relu2", "gelu_tanh") for bm in (64, 128)] + \
-        [(q, a, 256) for q in ("fp8_tensor", "w4a8") for a in ("silu", "relu2", "gelu_tanh")]
+        [(q, a, 256) for q in ("fp8_tensor", "w4a8") for a in ("silu", "relu2", "gelu_tanh")] + \
+        [(q, a, 128) for q in ("mxfp8", "mxfp4") for a in ("silu", "relu2", "gelu_tanh")]
 
 
 @pytest.mark.parametrize("quant,act,bm", TILED)

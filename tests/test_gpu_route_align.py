@@ -108,7 +108,7 @@ def _bf16_vals(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
-@pytest.mark.parametrize("quant", ["fp8_tensor", "fp8_block", "w4a8"])
+@pytest.mark.parametrize("quant", ["fp8_tensor", "fp8_block", "w4a8", "mxfp8"])
 @pytest.mark.parametrize("T,H", [(1, 2048), (37, 384), (256, 2048), (8192, 6144)])
 def test_quant_act_bitexact(quant, T, H):
     say(f"quant {quant} T={T} H={H}")
@@ -119,17 +119,21 @@ def test_quant_act_bitexact(quant, T, H):
         x[1, :16] = [1.0625, 1.1875, -1.0625, 3.0, 0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -10,
                      448.0, 500.0, -1e4, 1e-30, 0.5, 0.25, 7.0, -7.0]
         x[2] *= 1e3
+        x[3, 32:64] *= 1e-38                             # subnormal-range blocks
+        x[3, 64:96] *= 1e30
     bits = _bf16_bits(x)
     xv = _bf16_vals(bits)
     a1 = np.float32(1.0) if T > 3 else np.float32(np.abs(xv).max() / 448)  # 1.0: ties, saturation
     p = moe.problem(T=T, H=H, I=128, E_routed=8, top_k=2, quant=quant)
     xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
     xs = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+    if quant == "mxfp8":
+        xs = torch.empty((T, H // 32), dtype=torch.uint8, device="cuda")
     moe.moe_quant_act(p, dev(bits), torch.tensor(float(a1), device="cuda"), xq, xs)
     torch.cuda.synchronize()
     rq, rs = oracle.quant_x(xv.astype(np.float64), quant, a1)
     assert np.array_equal(xq.cpu().numpy(), rq)
-    if quant == "fp8_block":
+    if quant in ("fp8_block", "mxfp8"):
         assert np.array_equal(xs.cpu().numpy(), rs)
 
 
@@ -185,7 +189,10 @@ def test_prepare_route_align_bitexact(T, Er, k, ns, renorm, bm):
                                                ("w4a8", 64, 6144, 20, 8, 0),
                                                ("fp8_block", 300, 2048, 512, 10, 1),
                                                ("fp8_block", 4, 2048, 512, 10, 1),
-                                               ("w4a8", 8, 6144, 20, 8, 0)])
+                                               ("w4a8", 8, 6144, 20, 8, 0),
+                                               ("mxfp8", 8, 2048, 128, 8, 0),
+                                               ("mxfp4", 64, 2048, 128, 8, 0),
+                                               ("mxfp8", 300, 2048, 512, 10, 1)])
 def test_prepare_quantise_equals_separate_calls(quant, T, H, Er, k, ns):
     """moe_prepare's fused routing + quantisation + alignment is bit-identical
     to moe_route, moe_quant_act and moe_align called one after another."""
@@ -202,7 +209,9 @@ def test_prepare_quantise_equals_separate_calls(quant, T, H, Er, k, ns):
         return dict(ids=torch.empty((T, K), dtype=torch.int32, device="cuda"),
                     w=torch.empty((T, K), dtype=torch.float32, device="cuda"),
                     xq=torch.empty((T, H), dtype=torch.uint8, device="cuda"),
-                    xs=torch.zeros((T, H // 128), dtype=torch.float32, device="cuda"),
+                    xs=torch.zeros((T, H // 32), dtype=torch.uint8, device="cuda")
+                    if quant.startswith("mx") else
+                    torch.zeros((T, H // 128), dtype=torch.float32, device="cuda"),
                     si=torch.full((rows,), -7, dtype=torch.int32, device="cuda"),
                     be=torch.full((blocks,), -7, dtype=torch.int32, device="cuda"),
                     off=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
