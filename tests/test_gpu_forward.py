@@ -298,3 +298,38 @@ def test_mx_pack_scale_padding_and_swap(quant):
     torch.cuda.synchronize()
     ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"])
     assert_close(out.float().cpu().numpy(), ref, quant, f"{quant} swap+pad")
+
+
+@pytest.mark.parametrize("quant,T", [("bf16", 1), ("bf16", 97), ("fp8_block", 40), ("mxfp4", 128)])
+def test_forward_matches_components_with_duplicates_and_empty_tokens(quant, T):
+    """moe_forward is bit-identical to the separate entry points, call after
+    call, with the same expert twice within a token and tokens without a
+    valid slot (whose output rows are zero)."""
+    cfg = ad_hoc(96, quant, "silu", H=256, I=384, E_routed=12, top_k=4)
+    W = synth.make_weights(cfg, seed=123)
+    tok = synth.make_tokens(cfg, T, seed=124)
+    rng = np.random.default_rng(125)
+    ids = rng.integers(0, 12, (T, 4)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]                           # the same expert twice
+    ids[rng.random((T, 4)) < 0.2] = -1
+    ids[T // 2] = -1                                # no valid slot
+    w = rng.uniform(0.1, 1.0, (T, 4)).astype(np.float32)
+    layer = build_layer(cfg, W)
+    assert moe.block_m(layer.problem(T)) == 16
+    x, di, dw = dev(tok["x_bits"]), dev(ids), dev(w)
+    outs = []
+    for _ in range(3):
+        outs.append(layer.forward(x, None, di, dw).clone())
+    b = layer.buffers(T)
+    b["topk_ids"].copy_(di)
+    b["topk_w"].copy_(dw)
+    layer.align(T, b)
+    layer.quant(T, x, b)
+    layer.gemm1(T, x, b)
+    layer.gemm2(T, b)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), b["out"].view(torch.int16))
+    assert torch.count_nonzero(outs[0][T // 2].float()) == 0
+    ref = oracle_forward(cfg, W, tok["x_bits"], topk_ids=ids, topk_w=w.astype(np.float64))
+    assert_close(outs[0].float().cpu().numpy(), ref, quant, f"fused combine {quant} T={T}")
