@@ -131,8 +131,8 @@ typedef struct moe_problem {
   int32_t quant;        /* enum moe_quant                                        */
   int32_t block_m;      /* alignment block (rows per GEMM tile): 0 = library
                            choice, else 16, 64, 128 or 256 (256: fp8
-                           per-tensor and W4A8 modes only; the MX modes run
-                           16 and 128).  Every call of one
+                           per-tensor, W4A8 and MX modes only; the MX modes
+                           run 16, 128 and 256).  Every call of one
                            layer pass must see the same resolved value
                            (moe_block_m).                                        */
 } moe_problem;

@@ -238,12 +238,15 @@ template <int Q, int WC, int NWV, int WT = 4, int NW = 8> struct LdsCfg {
   static constexpr int A_BYTES = TILES * QT<Q>::FRAG;
   static constexpr int B_BYTES = NT * 2048;
   // scales of a stage: fp8 block / int4 group scales in 1 KiB; MX: E8M0
-  // weight scales (64 bytes per tile) then the token rows' (4 bytes per row,
-  // and as much again for the waves whose copies are not read)
-  static constexpr int SC_W8 = kMx<Q> ? TILES * 64 : 0;
+  // weight scales (64 bytes per tile; every wave loads 256 bytes per load
+  // round, the rounds' tail past the last tile is not read), then the token
+  // rows' (4 bytes per row, 64 rows per wave; the waves past the rows load
+  // copies that are not read)
+  static constexpr int MXW = kMx<Q> ? (TILES * 64 + NWV * 256 - 1) / (NWV * 256) : 0;
+  static constexpr int SC_W8 = MXW * NWV * 256;
   static constexpr int SC_BYTES = (Q == MOE_QUANT_FP8_BLOCK || Q == MOE_QUANT_W4A8) ? 1024
                                   : kMx<Q> ? SC_W8 + NWV * 256 : 0;
-  static constexpr int SC_LOADS = kMx<Q> ? SC_W8 / (NWV * 256) + 1 : (SC_BYTES ? 1 : 0);
+  static constexpr int SC_LOADS = kMx<Q> ? MXW + 1 : (SC_BYTES ? 1 : 0);
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   // stages: as many as fit, at most 4
 #ifdef MOE_LDS_MAX_STAGES
@@ -258,8 +261,8 @@ template <int Q, int WC, int NWV, int WT = 4, int NW = 8> struct LdsCfg {
   static_assert(Q != MOE_QUANT_FP8_BLOCK || WC == 1,
                 "block scales: one workgroup spans the 128 output channels of a group");
   static_assert(TILES % NWV == 0 && NT % NWV == 0, "whole fragments per wave");
-  static_assert(!kMx<Q> || (SC_W8 % (NWV * 256) == 0 && NT * 16 <= 128 && NWV >= 2),
-                "MX: whole 256-byte weight-scale loads per wave, token rows in two waves");
+  static_assert(!kMx<Q> || (TILES % 4 == 0 && NT * 16 % 64 == 0 && NT * 16 <= 64 * NWV),
+                "MX: whole 4-tile weight-scale loads, the token rows in 64-row loads");
 };
 
 // GEMM1 epilogue of the 8-wave fp8 per-tensor tile through the LDS: each
@@ -423,8 +426,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
     }
     // MX: the weight scales of tiles 4 (j NWV + wave) .. +3, 4 bytes per lane
     // (lane l: tile + l / 16, bytes 4 (l % 16) of the tile's 64); the token
-    // row scales (4 k-blocks, 4 bytes) of row 64 (wave % 2) + lane
-    constexpr int MXW = C::SC_LOADS - 1;  // weight-scale loads per wave
+    // row scales (4 k-blocks, 4 bytes) of row 64 (wave % (BM / 64)) + lane
+    constexpr int MXW = C::MXW;           // weight-scale loads per wave
     const uint8_t* mx_wsrc[MXW > 0 ? MXW : 1];
     const uint8_t* mx_tsrc = nullptr;
     if constexpr (MX) {
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
         const int t = min(wg_tile0 + 4 * (j * NWV + wave) + lane / 16, g.tiles - 1);
         mx_wsrc[j] = g.w_sc8 + (size_t(e) * g.tiles + t) * g.steps * 64 + (lane % 16) * 4;
       }
-      const int r = 64 * (wave % 2) + lane;
+      const int r = 64 * (wave % (BM / 64)) + lane;
       int brow;
       if (PHASE == 1) {
         const int f = r < BM ? g.sorted_ids[row0 + r] : g.A;
@@ -547,9 +550,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
             }
           }
         }
-        // 16 token tiles: keep each tile's LDS reads next to its MFMAs (read
-        // all ahead, their 128 registers and the accumulators do not fit)
-        if constexpr (NW > 8) __builtin_amdgcn_sched_barrier(0);
+        // 16 token tiles, or MX on 8 waves: keep each tile's LDS reads next to
+        // its MFMAs (read all ahead, they and the accumulators do not fit)
+        if constexpr (NW > 8 || (MX && NWV == 8)) __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -586,7 +589,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
     if (S > 3 && st + 2 < nst) step(std::integral_constant<int, 2 % S>{}, st + 2);
     // drain the surplus loads before the LDS is handed back
     wait_vm_then_barrier<0>();
-    if constexpr (NWV == 8 && WC == 2 && PHASE == 1) {
+    if constexpr (NWV == 8 && WC == 2 && PHASE == 1 && Q == MOE_QUANT_FP8_TENSOR) {
       static_assert(Q == MOE_QUANT_FP8_TENSOR && C::STAGE >= 128 * (256 + 16), "8-wave GEMM1 tile");
       lds_epilogue1<ACT, WT, NW>(g, acc, e, row0, wr, wc, ct, (nvalid + 15) >> 4, wg_tile0,
                                  active, lds_s0, lds_s1);
@@ -668,7 +671,7 @@ hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
           return hipGetLastError();
         }
       }
-      if constexpr (Q == MOE_QUANT_FP8_TENSOR) {
+      if constexpr (Q == MOE_QUANT_FP8_TENSOR || kMx<Q>) {
         // 8 waves, 256 x 256: one workgroup per tile (the persistent loop's
         // state does not fit the registers of 8 waves of 4 x 8 tiles)
         if (c.nt == 16 && c.kind == 2) {

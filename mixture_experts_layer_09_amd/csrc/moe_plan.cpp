@@ -151,12 +151,13 @@ int make_plan(const moe_problem* p, Plan* plan) {
   // ---- tile table: the alignment block follows the expected rows per
   // expert.  Decode-sized problems stream weights 16 token rows at a time;
   // with many rows per expert the tiled kernels stage 128 token rows in LDS
-  // and reuse every weight fragment across them; fp8 per-tensor and int4
+  // and reuse every weight fragment across them; fp8 per-tensor, int4 and MX
   // weights with 256 or more rows per expert take 256 token rows per block,
   // so that each weight byte brought into the LDS (and each int4 fragment
   // converted to e4m3) serves twice the tokens.
   const int64_t rows_per_expert = q.A / std::max(1, p->E);
-  const bool wide_ok = p->quant == MOE_QUANT_FP8_TENSOR || p->quant == MOE_QUANT_W4A8;
+  const bool wide_ok =
+      p->quant == MOE_QUANT_FP8_TENSOR || p->quant == MOE_QUANT_W4A8 || quant_is_mx(p->quant);
   if (p->block_m != 0) {
     q.BM = p->block_m;
   } else if (rows_per_expert >= MOE_WIDE_MIN_ROWS && wide_ok) {
@@ -168,9 +169,9 @@ int make_plan(const moe_problem* p, Plan* plan) {
   }
   if (q.BM == 256 && !wide_ok)
     return fail(MOE_ERR_UNSUPPORTED,
-                "block_m = 256 runs for the fp8 per-tensor and int4 (W4A8) modes only");
-  if (quant_is_mx(p->quant) && q.BM != 16 && q.BM != 128)
-    return fail(MOE_ERR_UNSUPPORTED, "the MX modes run block_m = 16 and 128");
+                "block_m = 256 runs for the fp8 per-tensor, int4 (W4A8) and MX modes only");
+  if (quant_is_mx(p->quant) && q.BM == 64)
+    return fail(MOE_ERR_UNSUPPORTED, "the MX modes run block_m = 16, 128 and 256");
   const int64_t nz = std::min<int64_t>(p->E, q.A);
   q.max_blocks = std::min<int64_t>(q.A, (q.A + nz * (q.BM - 1)) / q.BM);
   q.max_rows = q.max_blocks * q.BM;

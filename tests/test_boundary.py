@@ -68,7 +68,8 @@ def test_valid_problems(plan):
     (dict(quant=9), moe.MOE_ERR_INVALID_ARG),
     (dict(quant=6), moe.MOE_ERR_INVALID_ARG),
     (dict(quant="mxfp8", block_m=64), moe.MOE_ERR_UNSUPPORTED),   # MX: 16 or 128
-    (dict(quant="mxfp4", block_m=256), moe.MOE_ERR_UNSUPPORTED),
+    (dict(quant="mxfp4", block_m=64), moe.MOE_ERR_UNSUPPORTED),
+    (dict(quant="bf16", block_m=256), moe.MOE_ERR_UNSUPPORTED),
     (dict(quant="mxfp4", I=160), moe.MOE_ERR_ALIGNMENT),          # MX needs 128
     (dict(block_m=17), moe.MOE_ERR_INVALID_ARG),
     (dict(block_m=256), moe.MOE_ERR_UNSUPPORTED),                 # 256: fp8 per-tensor, W4A8

@@ -235,7 +235,8 @@ def test_invalid_call_enqueues_nothing():
 TILED = [(q, a, bm) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
          for a in ("silu", "relu2", "gelu_tanh") for bm in (64, 128)] + \
         [(q, a, 256) for q in ("fp8_tensor", "w4a8") for a in ("silu", "relu2", "gelu_tanh")] + \
-        [(q, a, 128) for q in ("mxfp8", "mxfp4") for a in ("silu", "relu2", "gelu_tanh")]
+        [(q, a, bm) for q in ("mxfp8", "mxfp4") for a in ("silu", "relu2", "gelu_tanh")
+         for bm in (128, 256)]
 
 
 @pytest.mark.parametrize("quant,act,bm", TILED)
@@ -257,10 +258,10 @@ def test_forward_tiled_ragged(quant, act, bm):
     assert_close(out.float().cpu().numpy(), ref, quant, f"tiled {quant} {act} bm={bm}")
 
 
-@pytest.mark.parametrize("quant,act", [(q, a) for q in ("fp8_tensor", "w4a8")
+@pytest.mark.parametrize("quant,act", [(q, a) for q in ("fp8_tensor", "w4a8", "mxfp8", "mxfp4")
                                        for a in ("silu", "relu2", "gelu_tanh")])
 def test_forward_wide_blocks_by_default(quant, act):
-    """fp8 per-tensor and int4 with 256+ rows per expert take 256-row blocks
+    """fp8 per-tensor, int4 and MX with 256+ rows per expert take 256-row blocks
     by themselves: several full blocks per expert, ragged last blocks, and
     blocks whose second half of token tiles is empty or partly filled."""
     cfg = ad_hoc(94, quant, act, H=512, I=384, E_routed=4, top_k=2, n_shared=1)
