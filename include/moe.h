@@ -73,7 +73,7 @@ typedef void* moe_stream_t; /* hipStream_t */
 enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* a size, enum or pointer is out of its domain  */
-  MOE_ERR_UNSUPPORTED = -2, /* a valid combination this build does not run   */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid combination the library does not run */
   MOE_ERR_ALIGNMENT = -3,   /* H or I breaks the alignment the formats need  */
   MOE_ERR_WORKSPACE = -4,   /* workspace / scratch smaller than required     */
   MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed           */
