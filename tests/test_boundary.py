@@ -148,3 +148,23 @@ def test_status_strings(plan):
 def test_single_hip_runtime():
     """The library binds to the HIP runtime torch brought into the process."""
     assert len(moe._hip_runtimes()) == 1
+
+
+@pytest.mark.parametrize("quant,src_I,status", [
+    ("mxfp8", 100, moe.MOE_ERR_ALIGNMENT),      # MX scales need src_I % 32 == 0
+    ("mxfp4", 200, moe.MOE_ERR_ALIGNMENT),
+    ("fp8_block", 448, moe.MOE_ERR_ALIGNMENT),  # block scales need src_I == I
+    ("w4a8", 384, moe.MOE_ERR_ALIGNMENT),
+    ("mxfp8", 0, moe.MOE_ERR_INVALID_ARG),
+    ("bf16", 513, moe.MOE_ERR_INVALID_ARG),     # src_I > I
+])
+def test_pack_rejects_source_sizes_before_launching(quant, src_I, status):
+    """The packers check src_I against the mode before anything reaches the
+    device (the pointers below are never dereferenced)."""
+    p = P(quant=quant)
+    dummy = ctypes.c_void_p(16)
+    assert moe.lib.moe_pack_w13(ctypes.byref(p), dummy, src_I, 0, dummy, dummy, dummy,
+                                None) == status
+    assert moe.lib.moe_pack_w2(ctypes.byref(p), dummy, src_I, dummy, dummy, dummy,
+                               None) == status
+    assert moe.lib.moe_last_error()
