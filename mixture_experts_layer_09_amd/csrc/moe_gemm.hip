@@ -6,9 +6,10 @@
 // over the gathered tokens; the packed W13 holds each group of 16 gate rows
 // next to its 16 up rows, so a wave computing a (gate, up) tile pair holds
 // gate channel c and up channel c in the same lane and register and applies
-// SiLU(gate) * up -- or relu(h)^2 for the non-gated layer (sglang PR 21321
-// page) -- before anything leaves registers; only the I activated columns are
-// stored, in the compute format.
+// SiLU(gate) * up or GELU_tanh(gate) * up (flashinfer PR 4329 page, sections
+// 1 and 3) -- or relu(h)^2 for the non-gated layer (sglang PR 21321 page) --
+// before anything leaves registers; only the I activated columns are stored,
+// in the compute format.
 // GEMM2 (flashinfer PR 4329 page, sections 3-4): y = W2[e] . a, scaled by the
 // routing weight, written per assignment in fp32; the combine then sums each
 // token's K' rows in slot order and rounds once to bf16.
@@ -18,7 +19,8 @@
 // tokens still streams whole weight rows through the matrix cores.  Weights
 // come straight from HBM into registers in 16-byte lane loads of pre-tiled
 // fragments (1 or 2 KiB per wave load); several k-steps of fragments are in
-// flight per wave.
+// flight per wave.  The MX modes feed each lane's E8M0 weight and token
+// scales to the scaled MFMA, which applies them per 32 k.
 #include "moe_device.hpp"
 #include "moe_gemm_common.hpp"
 #include "moe_launch.hpp"

@@ -1,9 +1,10 @@
 // Grouped expert GEMMs for prefill-sized batches (many tokens per expert).
 //
 // Same operation as the weight-streaming kernels in moe_gemm.hip -- GEMM1
-// with the SiLU*up / relu^2 epilogue on the 16-row gate/up interleave (sglang
-// PR 32944 page, sections 1-3; flashinfer PR 4329 page, section 2), GEMM2
-// with the routing weight -- tiled for reuse:
+// with the gated (SiLU or GELU_tanh of the gate, times up) or relu^2 epilogue
+// on the 16-row gate/up interleave (sglang PR 32944 page, sections 1-3;
+// flashinfer PR 4329 page, sections 1-3), GEMM2 with the routing weight --
+// tiled for reuse:
 //  * a workgroup of 4 waves takes one aligned block of BM = 16*NT token rows
 //    of one expert and a slice of 4*WT*16 weight rows; each wave owns WT
 //    16-row weight tiles (gate/up pairs for gated GEMM1) against all NT
