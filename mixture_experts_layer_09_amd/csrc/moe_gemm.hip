@@ -344,8 +344,10 @@ hipError_t dispatch_stream(const GemmCfg& c, dim3 grid, const GemmArgs& a, hipSt
     if (c.wt == 4 && c.ksplit == 1) gemm_stream<PHASE, Q, ACT, 4, 1><<<grid, block, 0, st>>>(a);
     else return hipErrorInvalidValue;
   } else if constexpr (kMx<Q>) {
-    // GEMM1: a wave's 4 tiles hold whole 32-channel scale blocks
+    // a wave's 4 tiles hold whole 32-channel scale blocks of GEMM1's output
     if (c.wt == 4 && c.ksplit == 4) gemm_stream<PHASE, Q, ACT, 4, 4><<<grid, block, 0, st>>>(a);
+    else if (c.wt == 4 && c.ksplit == 2) gemm_stream<PHASE, Q, ACT, 4, 2><<<grid, block, 0, st>>>(a);
+    else if (c.wt == 4 && c.ksplit == 1) gemm_stream<PHASE, Q, ACT, 4, 1><<<grid, block, 0, st>>>(a);
     else return hipErrorInvalidValue;
   } else {
     if (c.wt == 4 && c.ksplit == 1) gemm_stream<PHASE, Q, ACT, 4, 1><<<grid, block, 0, st>>>(a);
