@@ -69,3 +69,27 @@ def test_native_sources_do_not_reference_the_oracle():
         for f in files:
             txt = open(os.path.join(root, f)).read()
             assert "oracle" not in txt.lower(), f
+
+
+def test_weight_bytes_count_every_format_and_scale():
+    """Algorithmic bytes per expert: elements at the format's width plus its
+    scales (one fp32 per 128x128 block, one bf16 per row per 128 K, one E8M0
+    byte per row per 32 K)."""
+    import dataclasses
+    b = _bench_module()
+    cfg, _ = b.workload("cfg2_M64")                  # N1 = 1536, H = 2048, I = 768
+    n13, n2 = 1536 * 2048, 2048 * 768
+    want = {"bf16": (2 * n13, 2 * n2),
+            "fp8_tensor": (n13 + 4, n2 + 4),
+            "fp8_block": (n13 + 12 * 16 * 4, n2 + 16 * 6 * 4),
+            "w4a8": (n13 // 2 + 1536 * 16 * 2, n2 // 2 + 2048 * 6 * 2),
+            "mxfp8": (n13 + n13 // 32, n2 + n2 // 32),
+            "mxfp4": (n13 // 2 + n13 // 32, n2 // 2 + n2 // 32)}
+    for q, (w13, w2) in want.items():
+        assert b.weight_bytes_per_expert(dataclasses.replace(cfg, quant=q)) == (w13, w2), q
+
+
+def test_overridden_workloads_have_no_traffic_record():
+    b = _bench_module()
+    assert b.traffic_record("cfg2_M64_gelu_tanh") is None
+    assert b.traffic_record("cfg2_M64_mxfp4") is None
