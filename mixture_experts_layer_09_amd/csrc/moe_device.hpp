@@ -27,14 +27,27 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 // ---------------------------------------------------------------- MFMA
 // D[16x16] += A[16x128] * B[128x16] with one E8M0 scale per row / column and
 // 32 k (the OCP MX block): the scale of row (A) or column (B) r over k-block
-// kb comes from lane 16 kb + r (sa, sb: the lane's scale in the low byte).
-// FA, FB: element formats, 0 = e4m3, 4 = e2m1.  An e4m3 operand lane l
-// (g = l / 16) holds k 16g..16g+15 in bytes 0..15 and 64+16g..64+16g+15 in
-// bytes 16..31; an e2m1 operand holds k 32g..32g+31 as 32 nibbles (low
-// nibble first) in its first 16 bytes.
-template <int FA, int FB>
+// kb comes from lane 16 kb + r (sa: byte SA of the lane's register, sb: its
+// low byte).  FA, FB: element formats, 0 = e4m3, 4 = e2m1.  An e4m3 operand
+// lane l (g = l / 16) holds k 16g..16g+15 in bytes 0..15 and
+// 64+16g..64+16g+15 in bytes 16..31; an e2m1 operand holds k 32g..32g+31 as
+// 32 nibbles (low nibble first) in its first 16 bytes.
+template <int FA, int FB, int SA = 0>
 __device__ __forceinline__ f32x4 mfma_mx(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, SA, sa, 0, sb);
+}
+
+// The same with the A scale taken from byte `sel` (0..3, known once the
+// caller's loop is unrolled) of `sa`: four weight tiles' scales in one register.
+template <int FA, int FB>
+__device__ __forceinline__ f32x4 mfma_mx_sel(const i32x8& a, const i32x8& b, f32x4 c, int sa,
+                                             int sel, int sb) {
+  switch (sel) {
+    case 0: return mfma_mx<FA, FB, 0>(a, b, c, sa, sb);
+    case 1: return mfma_mx<FA, FB, 1>(a, b, c, sa, sb);
+    case 2: return mfma_mx<FA, FB, 2>(a, b, c, sa, sb);
+    default: return mfma_mx<FA, FB, 3>(a, b, c, sa, sb);
+  }
 }
 
 // D[16x16] += A[16x32] * B[32x16] in bf16.  Lane l holds row (A) / column

@@ -36,7 +36,7 @@ struct Stage {
   float ws[WT];    // FP8_BLOCK: weight block scale per tile
   f32x4 ws4[WT];   // W4A8: group scales of the lane's 4 rows per tile
   int bsc;         // MX: the lane's E8M0 B scale (its column, k-block l / 16)
-  int wsc[WT];     // MX: the lane's E8M0 weight scale per tile
+  int wsc4;        // MX: the lane's E8M0 weight scales of the 4 tiles, a byte each
 };
 }  // namespace
 
@@ -104,9 +104,8 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
     }
     if (MX) {
       S.bsc = g.b_sc8[size_t(brow) * (g.K / 32) + s * 4 + grp];
-#pragma unroll
-      for (int j = 0; j < WT; ++j)
-        S.wsc[j] = g.w_sc8[((size_t(e) * g.tiles + tile0 + j) * g.steps + s) * 64 + lane];
+      S.wsc4 = *reinterpret_cast<const int*>(
+          g.w_sc8 + (((size_t(e) * (g.tiles / 4) + tile0 / 4) * g.steps + s) * 64 + lane) * 4);
     }
   };
 
@@ -115,11 +114,12 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < WT; ++j) acc[j] = mfma_bf16(S.a[j][0], S.b[0], acc[j]);
     } else if (MX) {
+      static_assert(!MX || WT == 4, "MX: a wave's tiles are one 4-tile scale group");
       const i32x8 bb = fp8_pair(S.b[0], S.b[1]);
 #pragma unroll
       for (int j = 0; j < WT; ++j)
-        acc[j] = mfma_mx<kMxWFmt<Q>, 0>(mx_weight_operand<Q>(S.a[j][0], S.a[j][T::AV - 1]), bb,
-                                        acc[j], S.wsc[j], S.bsc);
+        acc[j] = mfma_mx_sel<kMxWFmt<Q>, 0>(mx_weight_operand<Q>(S.a[j][0], S.a[j][T::AV - 1]),
+                                            bb, acc[j], S.wsc4, j, S.bsc);
     } else {
       const i32x8 bb = fp8_pair(S.b[0], S.b[1]);
 #pragma unroll

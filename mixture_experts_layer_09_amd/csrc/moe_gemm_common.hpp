@@ -20,7 +20,7 @@ struct GemmArgs {
   uint8_t* out;              // GEMM1: a2 [rows][I]; GEMM2: y fp32 [A][H]
   float* out_scale;          // GEMM1 FP8_BLOCK: [rows][I/128]
   const uint8_t* b_sc8;      // MX: E8M0 per B row per 32 K
-  const uint8_t* w_sc8;      // MX: packed E8M0 weight scales [E][tiles][steps][64]
+  const uint8_t* w_sc8;      // MX: packed E8M0 weight scales [E][tiles/4][steps][64][4]
   uint8_t* out_sc8;          // GEMM1 MX: E8M0 [rows][I/32]
   int K, N, I, H, Kp, A, steps, tiles;
   int slices;                // tiled kernel: workgroups along the weight rows

@@ -429,17 +429,17 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       const int t = min(wg_tile0 + lane / 4, g.tiles - 1);
       ssrc = g.w_scale + (size_t(e) * g.tiles + t) * g.steps * 16 + (lane % 4) * 4;
     }
-    // MX: the weight scales of tiles 4 (j NWV + wave) .. +3, 4 bytes per lane
-    // (lane l: tile + l / 16, bytes 4 (l % 16) of the tile's 64); the token
-    // row scales (4 k-blocks, 4 bytes) of row 64 (wave % (BM / 64)) + lane
+    // MX: the weight scales of 4-tile group j NWV + wave of the workgroup
+    // (lane l: the dword of MFMA lane l, one byte per tile); the token row
+    // scales (4 k-blocks, 4 bytes) of row 64 (wave % (BM / 64)) + lane
     constexpr int MXW = C::MXW;           // weight-scale loads per wave
     const uint8_t* mx_wsrc[MXW > 0 ? MXW : 1];
     const uint8_t* mx_tsrc = nullptr;
     if constexpr (MX) {
 #pragma unroll
       for (int j = 0; j < MXW; ++j) {
-        const int t = min(wg_tile0 + 4 * (j * NWV + wave) + lane / 16, g.tiles - 1);
-        mx_wsrc[j] = g.w_sc8 + (size_t(e) * g.tiles + t) * g.steps * 64 + (lane % 16) * 4;
+        const int gq = min(wg_tile0 / 4 + j * NWV + wave, g.tiles / 4 - 1);
+        mx_wsrc[j] = g.w_sc8 + (size_t(e) * (g.tiles / 4) + gq) * g.steps * 256 + lane * 4;
       }
       const int r = 64 * (wave % (BM / 64)) + lane;
       int brow;
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       if constexpr (MX) {
   #pragma unroll
         for (int j = 0; j < MXW; ++j)
-          ld_lds4(mx_wsrc[j] + size_t(st) * 64,
+          ld_lds4(mx_wsrc[j] + size_t(st) * 256,
                   base + C::A_BYTES + C::B_BYTES + (j * NWV + wave) * 256);
         ld_lds4(mx_tsrc + st * 4, base + C::A_BYTES + C::B_BYTES + C::SC_W8 + wave * 256);
       }
@@ -509,11 +509,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       }
       float ws[WT];
       f32x4 ws4[WT];
-      int wsc[WT];
+      int wsc4 = 0;  // MX: this wave's 4 tiles' weight scales, a byte each
       if constexpr (MX) {
-        const int so = C::A_BYTES + C::B_BYTES + wr * WT * 64 + lane;
-  #pragma unroll
-        for (int r = 0; r < WT; ++r) wsc[r] = base[so + r * 64];
+        static_assert(!MX || WT == 4, "MX: a wave's tiles are one 4-tile scale group");
+        wsc4 = *reinterpret_cast<const int*>(base + C::A_BYTES + C::B_BYTES + wr * 256 + lane * 4);
       }
       if (Q == MOE_QUANT_FP8_BLOCK) {
   #pragma unroll
@@ -534,7 +533,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
                                  ((wc * NW + c) * 16 + lrow) * 4 + grp];
   #pragma unroll
             for (int r = 0; r < WT; ++r)
-              acc[r][c] = mfma_mx<kMxWFmt<Q>, 0>(a8[r], bb, acc[r][c], wsc[r], bsc);
+              acc[r][c] = mfma_mx_sel<kMxWFmt<Q>, 0>(a8[r], bb, acc[r][c], wsc4, r, bsc);
           } else if (Q == MOE_QUANT_FP8_TENSOR) {
   #pragma unroll
             for (int r = 0; r < WT; ++r) acc[r][c] = mfma_fp8(a8[r], bb, acc[r][c]);

@@ -25,9 +25,10 @@
 //             even k in the low nibble (the checkpoint's own nibble order);
 //  * block scales (fp8 128x128) keep the checkpoint's row order (the halves
 //    swapped when asked); int4 group scales become fp32 in packed row order,
-//    [E][tiles][steps][16]; MX E8M0 scales one byte per fragment lane,
-//    [E][tiles][steps][64], lane l holding the scale of row t*16 + l%16 over
-//    k-block 4s + l/16 (the lane that feeds it to the scaled MFMA).
+//    [E][tiles][steps][16]; MX E8M0 scales four tiles to a lane dword,
+//    [E][tiles/4][steps][64][4]: byte r of lane l's dword in group g is the
+//    scale of row (4g + r)*16 + l%16 over k-block 4s + l/16 (lane l feeds it
+//    to the scaled MFMA, which picks byte r with its operand select).
 #include "moe_device.hpp"
 #include "moe_launch.hpp"
 
@@ -157,19 +158,20 @@ __global__ void pack_group_scales(PackArgs a, const uint16_t* __restrict__ src,
   dst[i] = v;
 }
 
-// MX E8M0 scales (bytes [E][src_rows][src_K/32]) -> [E][tiles][steps][64]:
-// byte l of fragment (t, s) is the scale of packed row t*16 + l%16 over
-// k-block 4s + l/16.  Padding rows and columns take 127 (2^0; their weights
-// are zero).
+// MX E8M0 scales (bytes [E][src_rows][src_K/32]) -> [E][tiles/4][steps][64][4]:
+// byte 4l + j of (group g, step s) is the scale of packed row (4g + j)*16 +
+// l%16 over k-block 4s + l/16.  Padding rows and columns take 127 (2^0;
+// their weights are zero).
 __global__ void pack_mx_scales(PackArgs a, const uint8_t* __restrict__ src,
                                uint8_t* __restrict__ dst, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n) return;
-  const int l = int(i % 64);
-  const int s = int((i / 64) % a.steps);
-  const int64_t et = i / (64 * int64_t(a.steps));
-  const int tiles = a.rows / 16;
-  const int t = int(et % tiles), e = int(et / tiles);
+  const int j = int(i % 4);
+  const int l = int((i / 4) % 64);
+  const int s = int((i / 256) % a.steps);
+  const int64_t eg = i / (256 * int64_t(a.steps));
+  const int groups = a.rows / 64;
+  const int t = int(eg % groups) * 4 + j, e = int(eg / groups);
   const int r = t * 16 + l % 16, kb = 4 * s + l / 16;
   const int sr = a.which == 13 ? w13_src_row(a, r) : r;
   uint8_t v = 127;
