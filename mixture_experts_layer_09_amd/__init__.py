@@ -29,6 +29,9 @@ EXPORTS = (
     "moe_gemm1_act", "moe_gemm2_combine", "moe_forward",
 )
 HOST_ONLY = EXPORTS[:11]
+# measurement helpers declared in include/moe_probe.h (not part of the layer)
+PROBE_EXPORTS = ("moe_probe_read", "moe_probe_read_blocks", "moe_probe_mfma",
+                 "moe_probe_mfma_blocks", "moe_probe_mfma_flops")
 
 
 class MoEError(RuntimeError):
@@ -85,8 +88,13 @@ def _declare(lib, host_only=False):
                                              _VP, _VP, _VP, _VP, _SZ, _VP, _VP]),
         "moe_forward": (ctypes.c_int, [_P, ctypes.POINTER(Weights), _VP, _VP, _VP, _VP, _VP,
                                        _VP, _SZ, _VP]),
+        "moe_probe_read": (ctypes.c_int, [_VP, _SZ, _VP, _VP]),
+        "moe_probe_read_blocks": (_I32, []),
+        "moe_probe_mfma": (ctypes.c_int, [_I32, _I32, _VP, _VP]),
+        "moe_probe_mfma_blocks": (_I32, []),
+        "moe_probe_mfma_flops": (_I64, [_I32, _I32]),
     }
-    for name in (HOST_ONLY if host_only else EXPORTS):
+    for name in (HOST_ONLY if host_only else EXPORTS + PROBE_EXPORTS):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = sig[name]
     return lib
@@ -263,3 +271,17 @@ def moe_forward(p, w, x, logits, topk_ids, topk_w, out, ws, stream=None):
     return _check(lib.moe_forward(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(logits),
                                   _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws), nbytes,
                                   _stream(stream)), "moe_forward")
+
+
+# ------------------------------------------------------------------ measurement
+def probe_read(buf, sink, stream=None):
+    """One read-stream launch over the whole tensor `buf` (include/moe_probe.h)."""
+    return _check(lib.moe_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                     _stream(stream)), "moe_probe_read")
+
+
+def probe_mfma(dtype, iters, sink, stream=None):
+    """One dense MFMA-loop launch; dtype "bf16" or "fp8".  Returns its FLOPs."""
+    d = {"bf16": 0, "fp8": 1}[dtype]
+    _check(lib.moe_probe_mfma(d, iters, _ptr(sink), _stream(stream)), "moe_probe_mfma")
+    return lib.moe_probe_mfma_flops(d, iters)

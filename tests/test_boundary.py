@@ -33,6 +33,19 @@ def test_library_exports_every_symbol():
         assert hasattr(lib, name), name
 
 
+def test_measurement_helpers_declared_and_exported():
+    text = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(moe_probe_[a-z0-9_]+)\s*\(", text)))
+    assert declared == sorted(moe.PROBE_EXPORTS)
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    # argument checks happen before any launch
+    assert moe.lib.moe_probe_read(None, 16, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib.moe_probe_mfma(7, 1, ctypes.c_void_p(16), None) == moe.MOE_ERR_INVALID_ARG
+
+
 @pytest.fixture(scope="module")
 def plan():
     return moe.load_plan_lib()
