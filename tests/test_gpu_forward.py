@@ -154,7 +154,7 @@ def test_components_equal_forward():
 
 
 @pytest.mark.parametrize("quant,T", [("bf16", 29), ("fp8_block", 29), ("bf16", 13),
-                                     ("fp8_block", 13)])
+                                     ("fp8_block", 13), ("mxfp8", 29), ("mxfp4", 13)])
 def test_prerouted_with_masked_slots(quant, T):
     """Routing supplied by the caller; ids outside [0, E) contribute nothing."""
     cfg = ad_hoc(91, quant, "silu", H=256, I=256, E_routed=12, top_k=4)
@@ -334,3 +334,22 @@ def test_forward_matches_components_with_duplicates_and_empty_tokens(quant, T):
     assert torch.count_nonzero(outs[0][T // 2].float()) == 0
     ref = oracle_forward(cfg, W, tok["x_bits"], topk_ids=ids, topk_w=w.astype(np.float64))
     assert_close(outs[0].float().cpu().numpy(), ref, quant, f"fused combine {quant} T={T}")
+
+
+@pytest.mark.parametrize("quant,act", [("mxfp4", "gelu_tanh"), ("fp8_tensor", "gelu_tanh"),
+                                       ("mxfp8", "relu2")])
+def test_forward_without_renormalisation(quant, act):
+    """Routing weights taken from the softmax over all routed logits (no
+    renormalisation over the k picked), with a shared slot of gate 0.5."""
+    cfg = ad_hoc(97, quant, act, H=256, I=256, E_routed=16, top_k=3, n_shared=1,
+                 renormalize=False)
+    cfg = __import__("dataclasses").replace(cfg, shared_gate=0.5)
+    W = synth.make_weights(cfg, seed=321)
+    T = 45
+    tok = synth.make_tokens(cfg, T, seed=322)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
+    out = layer.forward(dev(tok["x_bits"]), dev(tok["logits"]))
+    torch.cuda.synchronize()
+    ref = oracle_forward(cfg, W, tok["x_bits"], tok["logits"], sc["a1"], sc["a2"])
+    assert_close(out.float().cpu().numpy(), ref, quant, f"no renorm {quant} {act}")
