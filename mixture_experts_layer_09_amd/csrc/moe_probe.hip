@@ -8,8 +8,11 @@
 //    eight independent accumulators per wave, all SIMDs busy.
 #include <atomic>
 
+#include <string>
+
 #include "../../include/moe_probe.h"
 #include "moe_device.hpp"
+#include "moe_plan.hpp"
 
 namespace moe {
 namespace {
@@ -100,11 +103,15 @@ extern "C" {
 int32_t moe_probe_read_blocks(void) { return moe::cu_count() * 8; }
 
 int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink, moe_stream_t stream) {
-  if (!buf || !sink || bytes % 16 != 0) return MOE_ERR_INVALID_ARG;
+  moe::clear_error();
+  if (!buf || !sink || bytes % 16 != 0)
+    return moe::fail(MOE_ERR_INVALID_ARG, "moe_probe_read: null pointer or bytes not a multiple of 16");
   (void)hipGetLastError();
   moe::probe_read_kernel<<<moe::cu_count() * 8, 256, 0, (hipStream_t)stream>>>(
       static_cast<const moe::u32x4*>(buf), int64_t(bytes / 16), sink);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return moe::fail(MOE_ERR_HIP, std::string("moe_probe_read: ") + hipGetErrorString(e));
+  return MOE_OK;
 }
 
 int32_t moe_probe_mfma_blocks(void) { return moe::cu_count() * 4; }
@@ -115,12 +122,16 @@ int64_t moe_probe_mfma_flops(int32_t dtype, int32_t iters) {
 }
 
 int moe_probe_mfma(int32_t dtype, int32_t iters, float* sink, moe_stream_t stream) {
-  if ((dtype != 0 && dtype != 1) || iters < 1 || !sink) return MOE_ERR_INVALID_ARG;
+  moe::clear_error();
+  if ((dtype != 0 && dtype != 1) || iters < 1 || !sink)
+    return moe::fail(MOE_ERR_INVALID_ARG, "moe_probe_mfma: dtype 0 or 1, iters >= 1, sink");
   (void)hipGetLastError();
   const dim3 grid(unsigned(moe::cu_count() * 4)), block(256);
   if (dtype == 1) moe::probe_mfma_kernel<1><<<grid, block, 0, (hipStream_t)stream>>>(iters, sink);
   else moe::probe_mfma_kernel<0><<<grid, block, 0, (hipStream_t)stream>>>(iters, sink);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return moe::fail(MOE_ERR_HIP, std::string("moe_probe_mfma: ") + hipGetErrorString(e));
+  return MOE_OK;
 }
 
 }  // extern "C"
