@@ -252,7 +252,7 @@ int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* sorted_ids
 
 /* Everything before GEMM1 in one call: moe_route (when logits is not NULL;
  * otherwise topk_ids is the caller's routing, an input), moe_quant_act (when
- * x is not NULL and the mode is fp8 / W4A8; a1_scale, xq, x_scale as there)
+ * x is not NULL and the mode is fp8 / W4A8 / MX; a1_scale, xq, x_scale as there)
  * and moe_align, with the arguments of those entry points.  Decode-sized
  * batches (T <= 128, T*K' <= 1024) route, align and -- up to 32768 elements
  * of x -- quantise in one kernel launch; larger ones run the separate
