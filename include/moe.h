@@ -9,9 +9,9 @@
  *   2. alignment : the T*K' (token, slot) assignments grouped by expert and
  *                  padded per expert to the GEMM row block (moe_align);
  *   3. GEMM1     : h = W13[e] . x[t] with the activation applied in the
- *                  epilogue -- SiLU(gate) * up for gated layers, relu(h)^2 for
- *                  non-gated ones -- storing only the I activated columns
- *                  (moe_gemm1_act);
+ *                  epilogue -- SiLU(gate) * up or GELU_tanh(gate) * up for
+ *                  gated layers, relu(h)^2 for non-gated ones -- storing only
+ *                  the I activated columns (moe_gemm1_act);
  *   4. GEMM2     : y = W2[e] . a, multiplied by the routing weight and summed
  *                  back into the token's row (moe_gemm2_combine);
  * and moe_forward runs all of it in one call.
@@ -22,11 +22,14 @@
  *             (hidden_states, w13/w2 and their scales, expert_weights, topk,
  *             renormalize, activation_type) and its bf16 output of the input's
  *             shape (section 1); _is_gated, _align_fp8_moe_weights, the
- *             [Up, Gate] -> [Gate, Up] swap, the fp8 scale scalars (section 2).
+ *             [Up, Gate] -> [Gate, Up] swap, the fp8 scale scalars,
+ *             _align_mxfp8_moe_weights (MXFP8 weights with [.., K/32] scales,
+ *             padded with them) (section 2).
  *   [GATED]   flashinfer PR 4329 page, "Gated MoE kernels for Blackwell":
- *             gated vs generic kernels chosen by activation (section 1), gate
- *             and up projections paired in FC1 (section 2), FC2 non-gated,
- *             routing and scatter unchanged (sections 3-4).
+ *             gated vs generic kernels chosen by activation, the gated
+ *             activations silu and gelu_tanh (sections 1 and 3), gate and up
+ *             projections paired in FC1 (section 2), FC2 non-gated, routing
+ *             and scatter unchanged (sections 3-4).
  *   [SHARED]  sglang PR 26204 page, "Qwen3-Next FP8 MoE: Shared-Expert
  *             Fusion": fp8 w8a8 with [128, 128] block scales, E = 513 slots
  *             (512 routed + the shared expert), BLOCK_SIZE_M per batch size
@@ -53,7 +56,8 @@
  *     at the caller's next synchronisation, as for any HIP kernel.
  *   - Sizes are int32; T*K'*max(H, I) must stay below 2^31.
  *   - Matrices are row-major.  bf16 values travel as uint16_t bit patterns and
- *     fp8 values as uint8_t OCP e4m3fn codes (bias 7, max 448, no infinities).
+ *     fp8 values as uint8_t OCP e4m3fn codes (bias 7, max 448, no infinities);
+ *     the MX modes' scales as uint8_t E8M0 codes (2^(c - 127), OCP MX v1.0).
  *   - Calls are reentrant; concurrent calls on different streams must not share
  *     output or workspace buffers.
  */
