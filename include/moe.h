@@ -60,6 +60,9 @@
  *     the MX modes' scales as uint8_t E8M0 codes (2^(c - 127), OCP MX v1.0).
  *   - Calls are reentrant; concurrent calls on different streams must not share
  *     output or workspace buffers.
+ *   - The device entry points enqueue kernels only (no allocation, memset,
+ *     copy or synchronisation; moe_pack_* with FP8_TENSOR scales aside, which
+ *     copies them), so a call can be captured into a HIP graph and replayed.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
