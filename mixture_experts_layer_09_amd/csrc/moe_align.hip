@@ -106,11 +106,15 @@ __device__ void padded_offsets(const int* cnt, int* off, int E, int BM, int* tmp
 }
 
 // Sentinels after each expert's real rows, and the expert of every block.
+// Sixteen lanes per expert, so that a long tail (up to BM - 1 sentinels)
+// is written by sixteen contiguous stores at a time rather than by one lane.
 __device__ void fill_tail(const int* cnt, const int* off, int E, int BM, int A,
                           int32_t* sorted_ids, int32_t* block_expert) {
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    for (int r = off[e] + cnt[e]; r < off[e + 1]; ++r) sorted_ids[r] = A;
-    for (int b = off[e] / BM; b < off[e + 1] / BM; ++b) block_expert[b] = e;
+  const int sub = threadIdx.x & 15;
+  for (int e = threadIdx.x >> 4; e < E; e += kThreads / 16) {
+    const int end = off[e + 1];
+    for (int r = off[e] + cnt[e] + sub; r < end; r += 16) sorted_ids[r] = A;
+    for (int b = off[e] / BM + sub; b < end / BM; b += 16) block_expert[b] = e;
   }
 }
 
@@ -362,7 +366,18 @@ __global__ __launch_bounds__(kThreads) void align_count(const int32_t* __restric
 }
 
 // One workgroup: totals, padded offsets, each chunk's base row per expert
-// (in place in hist), tails.  Shared memory: cnt[E], off[E+1], tmp.
+// (in place in hist), tails.  When the histograms fit (chunks * E <=
+// kScanStageInts) they are first copied into shared memory with all loads
+// in flight at once and scanned there, then written back row by row;
+// otherwise each thread walks its experts' columns in global memory.
+// Shared memory: cnt[E], off[E+1], tmp[kWaves+1] (+ the staged hist).
+constexpr int kScanStageInts = 32 * kThreads;
+
+size_t scan_lds_bytes(int chunks, int E) {
+  const size_t base = size_t(E) + (E + 1) + kWaves + 1;
+  return (base + (size_t(chunks) * E <= size_t(kScanStageInts) ? size_t(chunks) * E : 0)) * 4;
+}
+
 __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ hist, int chunks,
                                                        int A, int E, int BM,
                                                        int32_t* __restrict__ sorted_ids,
@@ -373,30 +388,66 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ his
   int* cnt = smem;
   int* off = cnt + E;
   int* tmp = off + E + 1;
-  // per expert, its chunks' counts: 8 independent loads in flight per pass
-  for (int x = threadIdx.x; x < E; x += kThreads) {
-    int run = 0;
-    for (int c0 = 0; c0 < chunks; c0 += 8) {
-      int v[8];
+  int* h = tmp + kWaves + 1;
+  if (int64_t(chunks) * E <= kScanStageInts) {
+    const int n = chunks * E;
+    {
+      int v[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = c0 + u < chunks ? hist[size_t(c0 + u) * E + x] : 0;
+      for (int u = 0; u < 32; ++u) {
+        const int i = threadIdx.x + u * kThreads;
+        v[u] = i < n ? hist[i] : 0;
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) run += v[u];
+      for (int u = 0; u < 32; ++u) {
+        const int i = threadIdx.x + u * kThreads;
+        if (i < n) h[i] = v[u];
+      }
     }
-    cnt[x] = run;
-  }
-  __syncthreads();
-  padded_offsets(cnt, off, E, BM, tmp, g_offsets, g_npad);
-  for (int x = threadIdx.x; x < E; x += kThreads) {
-    int run = off[x];
-    for (int c0 = 0; c0 < chunks; c0 += 8) {
-      int v[8];
+    __syncthreads();
+    for (int x = threadIdx.x; x < E; x += kThreads) {
+      int run = 0;
+      for (int c = 0; c < chunks; ++c) run += h[c * E + x];
+      cnt[x] = run;
+    }
+    __syncthreads();
+    padded_offsets(cnt, off, E, BM, tmp, g_offsets, g_npad);
+    for (int x = threadIdx.x; x < E; x += kThreads) {
+      int run = off[x];
+      for (int c = 0; c < chunks; ++c) {
+        const int v = h[c * E + x];
+        h[c * E + x] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kThreads) hist[i] = h[i];
+  } else {
+    // per expert, its chunks' counts: 8 independent loads in flight per pass
+    for (int x = threadIdx.x; x < E; x += kThreads) {
+      int run = 0;
+      for (int c0 = 0; c0 < chunks; c0 += 8) {
+        int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = c0 + u < chunks ? hist[size_t(c0 + u) * E + x] : 0;
+        for (int u = 0; u < 8; ++u) v[u] = c0 + u < chunks ? hist[size_t(c0 + u) * E + x] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (c0 + u < chunks) hist[size_t(c0 + u) * E + x] = run;
-        run += v[u];
+        for (int u = 0; u < 8; ++u) run += v[u];
+      }
+      cnt[x] = run;
+    }
+    __syncthreads();
+    padded_offsets(cnt, off, E, BM, tmp, g_offsets, g_npad);
+    for (int x = threadIdx.x; x < E; x += kThreads) {
+      int run = off[x];
+      for (int c0 = 0; c0 < chunks; c0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = c0 + u < chunks ? hist[size_t(c0 + u) * E + x] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (c0 + u < chunks) hist[size_t(c0 + u) * E + x] = run;
+          run += v[u];
+        }
       }
     }
   }
@@ -447,10 +498,12 @@ hipError_t launch_align(const moe_problem& p, const Plan& q, const int32_t* ids,
     return hipGetLastError();
   }
   align_count<<<q.chunks, kThreads, size_t(E) * 4, stream>>>(ids, A, E, scratch);
-  const size_t sm_scan = (size_t(E) + (E + 1) + kWaves + 1) * 4;
+  const size_t sm_scan = scan_lds_bytes(q.chunks, E);
+  hipError_t err = allow_lds(align_scan, sm_scan);
+  if (err != hipSuccess) return err;
   align_scan<<<1, kThreads, sm_scan, stream>>>(scratch, q.chunks, A, E, BM, sorted_ids,
                                                block_expert, offsets, num_padded);
-  hipError_t err = allow_lds(align_scatter, size_t(kWaves) * E * 4);
+  err = allow_lds(align_scatter, size_t(kWaves) * E * 4);
   if (err != hipSuccess) return err;
   align_scatter<<<q.chunks, kThreads, size_t(kWaves) * E * 4, stream>>>(ids, A, E, scratch,
                                                                           sorted_ids);

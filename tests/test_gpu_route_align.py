@@ -67,7 +67,9 @@ ALIGN_CASES = [  # T, K, E, kind
     (8192, 8, 20, "rand"), (8192, 6, 128, "rand"), (300, 4, 16, "skew"), (2000, 3, 64, "skew"),
     (100, 4, 32, "masked"), (3000, 5, 40, "masked"), (127, 3, 3, "rand"),
     # no tokens; 1024 experts with exactly one chunk of assignments, and one more
-    (0, 8, 128, "rand"), (1024, 1, 1024, "rand"), (1025, 1, 1024, "rand")]
+    (0, 8, 128, "rand"), (1024, 1, 1024, "rand"), (1025, 1, 1024, "rand"),
+    # chunk histograms of exactly the size scanned in shared memory, and past it
+    (32768, 1, 1024, "rand"), (33000, 1, 1024, "skew"), (40000, 1, 1024, "rand")]
 
 
 @pytest.mark.parametrize("T,K,E,kind", ALIGN_CASES)
