@@ -293,7 +293,11 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
 // out[t][:] = bf16(sum over valid slots j of y[t*K' + j][:]) with y in fp32,
 // one thread per 8 hidden values.  The rows of up to 8 slots are loaded
 // before any is added, so each thread has 16 loads in flight; the sum still
-// runs in slot order.
+// runs in slot order.  Every slot's row lies inside y, so the rows are
+// loaded together with the ids rather than after them; a slot whose id is
+// outside [0, E) (never written by GEMM2) is loaded and left out of the sum.
+// (4 or 16 values per thread, or plain instead of non-temporal loads, were
+// measured slower.)
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
                                                      const float* __restrict__ y,
                                                      uint16_t* __restrict__ out, int T, int H,
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       const int j = j0 + u;
       const int e = j < Kp ? ids[size_t(t) * Kp + j] : -1;
       ok[u] = e >= 0 && e < E;
-      if (ok[u]) {
+      if (j < Kp) {
         const float* row = y + (size_t(t) * Kp + j) * H + c;
         v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row));
         v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4));
