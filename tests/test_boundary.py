@@ -181,3 +181,19 @@ def test_pack_rejects_source_sizes_before_launching(quant, src_I, status):
     assert moe.lib.moe_pack_w2(ctypes.byref(p), dummy, src_I, dummy, dummy, dummy,
                                None) == status
     assert moe.lib.moe_last_error()
+
+
+def test_import_fails_without_the_library(tmp_path):
+    """The binding has no fallback: a copy of the package without libmoe.so
+    refuses to import."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "mixture_experts_layer_09_amd"
+    pkg.mkdir()
+    for name in ("__init__.py", "layer.py"):
+        shutil.copy(os.path.join(ROOT, "mixture_experts_layer_09_amd", name), pkg / name)
+    r = subprocess.run([sys.executable, "-c", "import mixture_experts_layer_09_amd"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libmoe.so is missing" in r.stderr
