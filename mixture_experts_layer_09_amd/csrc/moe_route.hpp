@@ -87,7 +87,8 @@ __device__ __forceinline__ float group_sum(float v) {
 // writes K' = top_k + n_shared ids and weights to ids_out / w_out (and the
 // ids to lds_ids when it is not null).  Called by all lanes of the group, with
 // every lane of the wave active.  `valid` false makes the group compute
-// without reading or writing (for the groups past the last token).
+// without writing (for the groups past the last token); `row` must still
+// point at a real row of Er logits.
 template <int L, int NPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, bool valid, int Er,
                                             int top_k, int n_shared, float shared_gate,
@@ -96,11 +97,20 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, bool 
   const int gl = threadIdx.x & (L - 1);  // lane within the group
   uint64_t key[NPL];
   float v[NPL];
+  // All NPL loads are issued before any is used: the index is clamped into
+  // the row (every lane, valid or not, reads inside a real row) rather than
+  // the load being predicated, which made the compiler wait for each load
+  // before issuing the next.
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int j = gl + L * i;
+    v[i] = row[j < Er ? j : Er - 1];
+  }
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int j = gl + L * i;
     const bool in = valid && j < Er;
-    v[i] = in ? row[j] : 0.f;
+    if (!in) v[i] = 0.f;
     key[i] = in ? (uint64_t(float_order_bits(v[i])) << 32) | uint32_t(~uint32_t(j)) : 0;
   }
   // Each lane sorts its keys (value's order bits, then the complemented
