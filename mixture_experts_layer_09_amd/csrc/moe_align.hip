@@ -29,13 +29,6 @@ namespace {
 constexpr int kThreads = kAlignChunk;  // 1024 threads, 16 waves
 constexpr int kWaves = kThreads / 64;
 
-// The decode prologue quantises x itself for up to this many passes of one
-// 8-element group per thread (beyond, a grid-wide quantisation launch).
-#ifndef MOE_FUSE_QUANT_MAX_PASSES
-#define MOE_FUSE_QUANT_MAX_PASSES 4
-#endif
-constexpr int kFuseQuantMaxPasses = MOE_FUSE_QUANT_MAX_PASSES;
-
 // Rank of this lane among the active lanes with the same expert below it, and
 // the number of active lanes with that expert.  The lanes sharing this lane's
 // expert are found with one ballot per bit of the expert id: a lane matches
@@ -183,9 +176,10 @@ __global__ __launch_bounds__(kThreads) void align_small(const int32_t* __restric
   align_in_block(sids, A, E, BM, smem + kThreads, sorted_ids, block_expert, g_offsets, g_npad);
 }
 
-// The decode-size prologue in one workgroup (T <= 128, T*K' <= 1024):
-// routing (groups of L lanes per token) or the caller's ids, the fp8
-// quantisation of x, then the alignment of the ids held in shared memory.
+// The decode-size prologue in one launch (T <= 128, T*K' <= 1024): routing
+// (groups of L lanes per token) or the caller's ids, then the alignment of
+// the ids held in shared memory, in one workgroup; the fp8 / MXFP8
+// quantisation of x in the launch's other workgroups.
 struct PrologueArgs {
   const float* logits;     // null: pre-routed, ids_in given
   const int32_t* ids_in;
@@ -204,23 +198,70 @@ struct PrologueArgs {
   void* xs;                // fp32 (QM 2) or E8M0 bytes (QM 3)
 };
 
-// QM: 0 no quantisation, 1 static per-tensor a1, 2 per token and 128 columns,
-// 3 MXFP8 per token and 32 columns.
+// One 8-element group of x per thread: i indexes the groups of x [T][H].
+// QM: 1 static per-tensor a1, 2 per token and 128 columns (a DPP row of 16
+// lanes is one group), 3 MXFP8 per token and 32 columns (a DPP quad).  Every
+// lane of the wave takes part in the reductions; lanes past the end hold 0.
+template <int QM>
+__device__ __forceinline__ void quant_group8(const PrologueArgs& a, int i) {
+  const bool in = int64_t(i) < int64_t(a.T) * a.H / 8;
+  const u32x4 v = in ? ld16(a.x + size_t(i) * 8) : u32x4{0, 0, 0, 0};
+  float f[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = bf16_to_f32(v[k] & 0xFFFFu);
+    f[2 * k + 1] = bf16_to_f32(v[k] >> 16);
+    amax = fmaxf(amax, fmaxf(fabsf(f[2 * k]), fabsf(f[2 * k + 1])));
+  }
+  float s = QM == 1 ? *a.a1 : 1.f;
+  if (QM >= 2) {
+    amax = fmaxf(amax, __uint_as_float(dpp<kDppXor1, 0xF>(0u, __float_as_uint(amax))));
+    amax = fmaxf(amax, __uint_as_float(dpp<kDppXor2, 0xF>(0u, __float_as_uint(amax))));
+  }
+  if (QM == 3) {
+    const int X = mx8_exponent(amax);
+    if (in) {
+      u32x2 o;
+      o[0] = mx8x4(f[0], f[1], f[2], f[3], X);
+      o[1] = mx8x4(f[4], f[5], f[6], f[7], X);
+      *reinterpret_cast<u32x2*>(a.xq + size_t(i) * 8) = o;
+      if ((threadIdx.x & 3) == 0) static_cast<uint8_t*>(a.xs)[i / 4] = uint8_t(X + 127);
+    }
+    return;
+  }
+  if (QM == 2) {
+    amax = fmaxf(amax, __uint_as_float(dpp<kDppHalfMirror, 0xF>(0u, __float_as_uint(amax))));
+    amax = fmaxf(amax, __uint_as_float(dpp<kDppMirror, 0xF>(0u, __float_as_uint(amax))));
+    s = amax > 0.f ? amax / 448.f : 1.f;
+  }
+  if (in) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) f[k] = f[k] / s;
+    u32x2 o;
+    o[0] = e4m3x4(f[0], f[1], f[2], f[3]);
+    o[1] = e4m3x4(f[4], f[5], f[6], f[7]);
+    *reinterpret_cast<u32x2*>(a.xq + size_t(i) * 8) = o;
+    if (QM == 2 && (threadIdx.x & 15) == 0) static_cast<float*>(a.xs)[i / 16] = s;
+  }
+}
+
+// Workgroup 0 routes (groups of L lanes per token) or takes the caller's ids,
+// then aligns them in shared memory; with QM != 0, workgroups 1.. quantise x
+// at the same time, one 8-element group per thread (neither part reads what
+// the other writes).
 template <int L, int NPL, int QM>
 __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
   extern __shared__ int smem[];
+  if constexpr (QM != 0) {
+    if (blockIdx.x > 0) {  // uniform per workgroup: no barrier below is reached
+      quant_group8<QM>(a, int(blockIdx.x - 1) * kThreads + int(threadIdx.x));
+      return;
+    }
+  }
   int* sids = smem;
   const int Kp = a.top_k + a.n_shared;
   const int wave = threadIdx.x >> 6;
-  // x for the quantisation is loaded first, so that its memory latency
-  // overlaps the routing's
-  const int n8 = QM != 0 ? a.T * a.H / 8 : 0;
-  u32x4 xv[QM != 0 ? kFuseQuantMaxPasses : 1];
-#pragma unroll
-  for (int q = 0; q < (QM != 0 ? kFuseQuantMaxPasses : 0); ++q) {
-    const int i = q * kThreads + threadIdx.x;
-    xv[q] = i < n8 ? ld16(a.x + size_t(i) * 8) : u32x4{0, 0, 0, 0};
-  }
   if (a.logits) {
     constexpr int TPW = 64 / L;
     for (int base = 0; base < a.T; base += kWaves * TPW) {
@@ -236,55 +277,6 @@ __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
     }
   } else {
     for (int f = threadIdx.x; f < a.T * Kp; f += kThreads) sids[f] = a.ids_in[f];
-  }
-  if (QM != 0) {
-    // 8 elements per thread and pass; a DPP row of 16 lanes is one 128-column group
-    const float s1 = QM == 1 ? *a.a1 : 1.f;
-#pragma unroll
-    for (int q = 0; q < kFuseQuantMaxPasses; ++q) {
-      const int i = q * kThreads + threadIdx.x;
-      const bool in = i < n8;
-      const u32x4 v = xv[q];
-      float f[8];
-      float amax = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        f[2 * k] = bf16_to_f32(v[k] & 0xFFFFu);
-        f[2 * k + 1] = bf16_to_f32(v[k] >> 16);
-        amax = fmaxf(amax, fmaxf(fabsf(f[2 * k]), fabsf(f[2 * k + 1])));
-      }
-      float s = s1;
-      if (QM >= 2) {
-        amax = fmaxf(amax, __uint_as_float(dpp<kDppXor1, 0xF>(0u, __float_as_uint(amax))));
-        amax = fmaxf(amax, __uint_as_float(dpp<kDppXor2, 0xF>(0u, __float_as_uint(amax))));
-      }
-      if (QM == 3) {
-        // 4 lanes (a DPP quad) are one 32-column block
-        const int X = mx8_exponent(amax);
-        if (in) {
-          u32x2 o;
-          o[0] = mx8x4(f[0], f[1], f[2], f[3], X);
-          o[1] = mx8x4(f[4], f[5], f[6], f[7], X);
-          *reinterpret_cast<u32x2*>(a.xq + size_t(i) * 8) = o;
-          if ((threadIdx.x & 3) == 0) static_cast<uint8_t*>(a.xs)[i / 4] = uint8_t(X + 127);
-        }
-        continue;
-      }
-      if (QM == 2) {
-        amax = fmaxf(amax, __uint_as_float(dpp<kDppHalfMirror, 0xF>(0u, __float_as_uint(amax))));
-        amax = fmaxf(amax, __uint_as_float(dpp<kDppMirror, 0xF>(0u, __float_as_uint(amax))));
-        s = amax > 0.f ? amax / 448.f : 1.f;
-      }
-      if (in) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) f[k] = f[k] / s;
-        u32x2 o;
-        o[0] = e4m3x4(f[0], f[1], f[2], f[3]);
-        o[1] = e4m3x4(f[4], f[5], f[6], f[7]);
-        *reinterpret_cast<u32x2*>(a.xq + size_t(i) * 8) = o;
-        if (QM == 2 && (threadIdx.x & 15) == 0) static_cast<float*>(a.xs)[i / 16] = s;
-      }
-    }
   }
   __syncthreads();
   align_in_block(sids, a.T * Kp, a.E, a.BM, smem + kThreads, a.sorted_ids, a.block_expert,
@@ -514,11 +506,13 @@ namespace {
 template <int L, int QM>
 hipError_t prologue_l(const PrologueArgs& a, size_t sm, hipStream_t stream) {
   const int npl = (a.Er + L - 1) / L;
+  const int64_t groups = QM != 0 ? int64_t(a.T) * a.H / 8 : 0;
+  const unsigned grid = 1u + unsigned((groups + kThreads - 1) / kThreads);
 #define MOE_PRO(N)                                                                 \
   do {                                                                             \
     hipError_t err = allow_lds(prologue_small<L, N, QM>, sm);                      \
     if (err != hipSuccess) return err;                                             \
-    prologue_small<L, N, QM><<<1, kThreads, sm, stream>>>(a);                      \
+    prologue_small<L, N, QM><<<grid, kThreads, sm, stream>>>(a);                   \
   } while (0)
   if (npl <= 1) MOE_PRO(1);
   else if (npl <= 2) MOE_PRO(2);
@@ -546,16 +540,6 @@ hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* log
                            uint8_t* xq, void* xs, bool quantise, int32_t* sorted_ids,
                            int32_t* block_expert, int32_t* offsets, int32_t* num_padded,
                            int32_t* scratch, hipStream_t stream) {
-  // The single-workgroup prologue quantises x in passes of one 8-element
-  // group per thread; past a few passes a grid-wide quantisation launch is
-  // faster than the serial loop.
-  const bool fuse_quant =
-      quantise && int64_t(p.T) * p.H <= int64_t(kFuseQuantMaxPasses) * kThreads * 8;
-  if (quantise && !fuse_quant && prologue_fits(p, q)) {
-    hipError_t err = launch_quant_act(p, x, a1, xq, xs, stream);
-    if (err != hipSuccess) return err;
-    quantise = false;
-  }
   if (!prologue_fits(p, q)) {
     hipError_t err = hipSuccess;
     if (logits) err = launch_route(p, logits, ids, w, stream);
