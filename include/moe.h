@@ -261,9 +261,9 @@ int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* sorted_ids
  * otherwise topk_ids is the caller's routing, an input), moe_quant_act (when
  * x is not NULL and the mode is fp8 / W4A8 / MX; a1_scale, xq, x_scale as there)
  * and moe_align, with the arguments of those entry points.  Decode-sized
- * batches (T <= 128, T*K' <= 1024) route, align and -- up to 32768 elements
- * of x -- quantise in one kernel launch; larger ones run the separate
- * kernels.  Outputs are bit-identical to the separate calls. */
+ * batches (T <= 128, T*K' <= 1024) route, align and quantise in one kernel
+ * launch (the quantisation in workgroups of their own); larger ones run the
+ * separate kernels.  Outputs are bit-identical to the separate calls. */
 int moe_prepare(const moe_problem* p, const float* logits, int32_t* topk_ids, float* topk_w,
                 const uint16_t* x, const float* a1_scale, uint8_t* xq, void* x_scale,
                 int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
