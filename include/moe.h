@@ -54,7 +54,8 @@
  *     failure returns MOE_ERR_HIP.  moe_last_error() gives a detail string for
  *     the last failing call on the calling thread.  Device-side faults surface
  *     at the caller's next synchronisation, as for any HIP kernel.
- *   - Sizes are int32; T*K'*max(H, I) must stay below 2^31.
+ *   - Sizes are int32; H and I are at most 2^20 and T*K'*max(H, I) must stay
+ *     below 2^31 (MOE_ERR_UNSUPPORTED otherwise).
  *   - Matrices are row-major.  bf16 values travel as uint16_t bit patterns and
  *     fp8 values as uint8_t OCP e4m3fn codes (bias 7, max 448, no infinities);
  *     the MX modes' scales as uint8_t E8M0 codes (2^(c - 127), OCP MX v1.0).

@@ -29,10 +29,6 @@
 #include "moe_launch.hpp"
 #include "moe_tile_common.hpp"
 
-#ifndef MOE_MX_SCHED_EVERY
-#define MOE_MX_SCHED_EVERY 2  // MX on 8 waves: a scheduling barrier after every Nth token tile
-#endif
-
 namespace moe {
 
 template <int PHASE, int Q, int ACT, int WT, int NT>
@@ -254,11 +250,7 @@ template <int Q, int WC, int NWV, int WT = 4, int NW = 8> struct LdsCfg {
   static constexpr int SC_LOADS = kMx<Q> ? MXW + 1 : (SC_BYTES ? 1 : 0);
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   // stages: as many as fit, at most 4
-#ifdef MOE_LDS_MAX_STAGES
-  static constexpr int SMAX = MOE_LDS_MAX_STAGES;
-#else
   static constexpr int SMAX = 4;
-#endif
   static constexpr int S = (160 * 1024 - 4096) / STAGE < SMAX ? (160 * 1024 - 4096) / STAGE : SMAX;
   // loads per wave per stage: weight fragments, token fragments, scales
   static constexpr int LOADS = TILES * QT<Q>::AV / NWV + NT * 2 / NWV + SC_LOADS;
@@ -558,9 +550,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
         // (MX: of each pair of tiles) next to their MFMAs (read all ahead,
         // they and the accumulators do not fit; MX pairs measured 1-2% faster
         // than single tiles, groups of 4 spill)
-        if constexpr (NW > 8 || (MX && NWV == 8 && MOE_MX_SCHED_EVERY > 0)) {
-          if (c % (NW > 8 ? 1 : MOE_MX_SCHED_EVERY) == (NW > 8 ? 0 : MOE_MX_SCHED_EVERY - 1))
-            __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NW > 8 || (MX && NWV == 8)) {
+          if (NW > 8 || c % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
     };

@@ -20,27 +20,18 @@ bool quant_is_fp8_act(int q) { return q != MOE_QUANT_BF16; }
 // workgroup with K split over its four waves, GEMM2 (shorter K) as 64 rows
 // with K split four ways.  The fp8 block-scaled GEMM1 keeps 128 output
 // channels (256 interleaved rows) in one workgroup, since the group maximum
-// of its quantised output spans them.  MOE_STREAM_FORCE_G1 / _G2 pick another
-// shape at build time (index into the table) for tuning builds.
-#ifndef MOE_WIDE_MIN_ROWS
-#define MOE_WIDE_MIN_ROWS 256
-#endif
-#ifndef MOE_LDS_KIND
-#define MOE_LDS_KIND 3
-#endif
-#ifndef MOE_STREAM_FORCE_G1
-#define MOE_STREAM_FORCE_G1 3
-#endif
-#ifndef MOE_STREAM_FORCE_G2
-#define MOE_STREAM_FORCE_G2 2
-#endif
-const GemmCfg kStreamShapes[] = {
-    {0, 1, 4, 1, 4}, {0, 1, 4, 2, 4}, {0, 1, 4, 4, 4}, {0, 1, 2, 4, 4},
-    {0, 1, 2, 2, 4}, {0, 1, 2, 1, 4}};
-GemmCfg stream_shape(int phase, bool fp8_block) {
-  if (phase == 1) return fp8_block ? kStreamShapes[0] : kStreamShapes[MOE_STREAM_FORCE_G1];
-  return kStreamShapes[MOE_STREAM_FORCE_G2];
-}
+// of its quantised output spans them.  {kind, nt, wt, ksplit, waves}.
+constexpr GemmCfg kStreamG1{0, 1, 2, 4, 4};
+constexpr GemmCfg kStreamG2{0, 1, 4, 4, 4};
+constexpr GemmCfg kStreamG1Fp8Block{0, 1, 4, 1, 4};
+// MX GEMM1: a wave's 4 tiles are whole 32-channel scale blocks of the output;
+// K split 4 ways for e4m3 weights, 2 ways for the half-size e2m1 fragments
+// (measured: MXFP4 at M = 64 39.7 vs 46.6 us, MXFP8 70.7 vs 76.7)
+constexpr GemmCfg kStreamG1Mxfp8{0, 1, 4, 4, 4};
+constexpr GemmCfg kStreamG1Mxfp4{0, 1, 4, 2, 4};
+// Rows per expert from which fp8 per-tensor, int4 and MX weights take
+// 256-row blocks.
+constexpr int64_t kWideMinRows = 256;
 }  // namespace
 
 int fail(int status, const std::string& msg) {
@@ -69,6 +60,7 @@ int32_t padded_intermediate(int32_t I, int32_t act, int32_t quant) {
   // k-step, block scale and group scale cover 128
   int32_t k = quant == MOE_QUANT_BF16 ? 32 : 128;
   int32_t m = std::max(a, k);  // both are powers of two
+  if (I > kMaxDim) return MOE_ERR_UNSUPPORTED;
   return (I + m - 1) / m * m;
 }
 
@@ -113,6 +105,8 @@ int make_plan(const moe_problem* p, Plan* plan) {
     return fail(MOE_ERR_INVALID_ARG, "unknown quant mode");
   if (p->T < 0 || p->H <= 0 || p->I <= 0)
     return fail(MOE_ERR_INVALID_ARG, "T must be >= 0, H and I > 0");
+  if (p->H > kMaxDim || p->I > kMaxDim)
+    return fail(MOE_ERR_UNSUPPORTED, "H and I must be at most 2^20");
   if (p->E_routed < 1 || p->n_shared < 0 || p->E != p->E_routed + p->n_shared)
     return fail(MOE_ERR_INVALID_ARG, "need E_routed >= 1, n_shared >= 0, E == E_routed + n_shared");
   if (p->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "at most 1024 expert slots");
@@ -160,7 +154,7 @@ int make_plan(const moe_problem* p, Plan* plan) {
       p->quant == MOE_QUANT_FP8_TENSOR || p->quant == MOE_QUANT_W4A8 || quant_is_mx(p->quant);
   if (p->block_m != 0) {
     q.BM = p->block_m;
-  } else if (rows_per_expert >= MOE_WIDE_MIN_ROWS && wide_ok) {
+  } else if (rows_per_expert >= kWideMinRows && wide_ok) {
     q.BM = 256;
   } else if (rows_per_expert >= kTiledMinRows) {
     q.BM = 128;
@@ -186,25 +180,20 @@ int make_plan(const moe_problem* p, Plan* plan) {
   q.ksteps_i = p->I / q.kstep;
   q.a2_elem = p->quant == MOE_QUANT_BF16 ? 2 : 1;
   if (q.BM == 16) {
-    q.g1 = stream_shape(1, p->quant == MOE_QUANT_FP8_BLOCK);
-    q.g2 = stream_shape(2, false);
-    // MX GEMM1: a wave's 4 tiles are whole 32-channel scale blocks of the
-    // output; K split 4 ways for e4m3 weights, 2 ways for the half-size e2m1
-    // fragments (measured: MXFP4 at M = 64 39.7 vs 46.6 us, MXFP8 70.7 vs 76.7)
-    if (quant_is_mx(p->quant))
-      q.g1 = kStreamShapes[p->quant == MOE_QUANT_MXFP4 ? 1 : 2];
+    q.g1 = p->quant == MOE_QUANT_FP8_BLOCK ? kStreamG1Fp8Block
+           : p->quant == MOE_QUANT_MXFP8   ? kStreamG1Mxfp8
+           : p->quant == MOE_QUANT_MXFP4   ? kStreamG1Mxfp4
+                                           : kStreamG1;
+    q.g2 = kStreamG2;
   } else {
-    // fp8 / int4 weights at 128-row blocks: weights and tokens staged in LDS by
-    // direct-to-LDS loads, several k-steps in flight, one persistent
-    // workgroup per CU taking the tiles in rounds (MOE_LDS_KIND 2 at build
-    // time: one workgroup per tile).  256-row blocks: 8 waves; fp8 one
-    // workgroup per tile, int4 persistent.
+    // fp8 / int4 / MX weights at 128-row blocks: weights and tokens staged in
+    // LDS by direct-to-LDS loads, several k-steps in flight, one persistent
+    // workgroup per CU taking the tiles in rounds (kind 3).  256-row blocks:
+    // 8 waves; int4 persistent, fp8 per-tensor and MX one workgroup per tile
+    // (kind 2).  bf16 weights: the register-staged tile (kind 1).
     const bool lds = q.BM >= 128 && p->quant != MOE_QUANT_BF16;
-#ifndef MOE_WIDE_KIND_W4A8
-#define MOE_WIDE_KIND_W4A8 3
-#endif
-    const int wide_kind = p->quant == MOE_QUANT_W4A8 ? MOE_WIDE_KIND_W4A8 : 2;
-    q.g1 = GemmCfg{lds ? (q.BM == 256 ? wide_kind : MOE_LDS_KIND) : 1, q.BM / 16, 4, 1, 4};
+    const int wide_kind = p->quant == MOE_QUANT_W4A8 ? 3 : 2;
+    q.g1 = GemmCfg{lds ? (q.BM == 256 ? wide_kind : 3) : 1, q.BM / 16, 4, 1, 4};
     q.g2 = q.g1;
   }
 

@@ -17,6 +17,7 @@ constexpr int kMaxRouted = 1024;   // logits per token the routing kernel holds
 constexpr int kMaxSlots = 64;      // K' = top_k + n_shared limit (one lane each)
 constexpr int kTiledMinRows = 48;  // rows per expert from which the tiled GEMMs run
 constexpr int kMxBlock = 32;       // elements per E8M0 scale in the MX modes
+constexpr int kMaxDim = 1 << 20;   // largest H and I (keeps 2I and padding in int32)
 
 // The OCP MX modes (E8M0 scales per 32 K on weights and activations).
 inline bool quant_is_mx(int q) { return q == MOE_QUANT_MXFP8 || q == MOE_QUANT_MXFP4; }
