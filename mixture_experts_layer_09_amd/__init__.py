@@ -205,72 +205,238 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _dtypes():
+    import torch
+    bf16 = (torch.bfloat16, torch.int16, torch.uint16)
+    u8 = (torch.uint8, torch.int8, torch.float8_e4m3fn)
+    return dict(bf16=bf16, u8=u8, f32=(torch.float32,), i32=(torch.int32,))
+
+
+class _Args:
+    """Collects the device pointers of one call after checking what the kernels
+    assume of each tensor: a torch tensor of the expected element type,
+    contiguous, at least `nbytes` bytes; `on_gpu()` then checks that every one
+    lives on a GPU.  Raises ValueError / TypeError before anything reaches the
+    library (the C ABI sees raw pointers and cannot check sizes)."""
+
+    def __init__(self):
+        self.tensors = []
+
+    def __call__(self, t, name, nbytes, kind=None, required=True):
+        import torch
+        if t is None:
+            if required:
+                raise ValueError(f"{name} is required")
+            return None
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+        if kind is not None and t.dtype not in _dtypes()[kind]:
+            raise ValueError(f"{name} has dtype {t.dtype}; expected one of "
+                             f"{', '.join(str(d) for d in _dtypes()[kind])}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise ValueError(f"{name} holds {have} bytes; the problem needs {int(nbytes)}")
+        self.tensors.append((name, t))
+        return t.data_ptr()
+
+    def on_gpu(self):
+        for name, t in self.tensors:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be on a GPU device, not {t.device}")
+
+
+def _shape(p):
+    """Sizes of the problem's buffers (raises MoEError for an invalid problem)."""
+    _check(validate(p), "moe_validate")
+    K = p.top_k + p.n_shared
+    q = p.quant
+    return dict(T=p.T, H=p.H, I=p.I, E=p.E, Er=p.E_routed, K=K, A=p.T * K, q=q,
+                rows=max_padded_rows(p), blocks=max_blocks(p),
+                a2_el=2 if q == QUANT["bf16"] else 1,
+                xs=(p.T * (p.H // 128) * 4 if q == QUANT["fp8_block"]
+                    else p.T * (p.H // 32) if q in (QUANT["mxfp8"], QUANT["mxfp4"]) else 0),
+                a2s_row=((p.I // 128) * 4 if q == QUANT["fp8_block"]
+                         else p.I // 32 if q in (QUANT["mxfp8"], QUANT["mxfp4"]) else 0))
+
+
+def _static_scales(q):
+    return q in (QUANT["fp8_tensor"], QUANT["w4a8"])
+
+
+def _routing_args(a, s, topk_ids, topk_w, required=True):
+    return (a(topk_ids, "topk_ids", s["A"] * 4, "i32", required),
+            a(topk_w, "topk_w", s["A"] * 4, "f32", required))
+
+
+def _block_args(a, s, sorted_ids, block_expert, num_padded):
+    """The alignment's outputs the GEMMs read."""
+    real = s["A"] > 0
+    return (a(sorted_ids, "sorted_ids", s["rows"] * 4, "i32", real),
+            a(block_expert, "block_expert", s["blocks"] * 4, "i32", real),
+            a(num_padded, "num_padded", 4, "i32", real))
+
+
+def _align_args(a, s, sorted_ids, block_expert, expert_offsets, num_padded):
+    """The alignment's outputs, in moe_align's argument order."""
+    real = s["A"] > 0
+    return (a(sorted_ids, "sorted_ids", s["rows"] * 4, "i32", real),
+            a(block_expert, "block_expert", s["blocks"] * 4, "i32", real),
+            a(expert_offsets, "expert_offsets", (s["E"] + 1) * 4, "i32"),
+            a(num_padded, "num_padded", 4, "i32"))
+
+
+def _x_args(a, s, x, a1_scale, xq, x_scale):
+    """x (bf16), and the quantised copy the fp8 / W4A8 / MX modes make of it."""
+    q = s["q"]
+    xp = a(x, "x", s["T"] * s["H"] * 2, "bf16", s["T"] > 0)
+    if q == QUANT["bf16"] or x is None:
+        return xp, None, None, None
+    return (xp, a(a1_scale, "a1_scale", 4, "f32", _static_scales(q)),
+            a(xq, "xq", s["T"] * s["H"], "u8"),
+            a(x_scale, "x_scale", s["xs"], None, s["xs"] > 0))
+
+
+def _src_bytes(p, which, src_I):
+    """Bytes of a checkpoint-layout weight and of its scales (moe_pack_w13/w2)."""
+    q, gated = p.quant, p.act != ACT["relu2"]
+    n = (2 * src_I if gated else src_I) if which == 13 else p.H
+    k = p.H if which == 13 else src_I
+    el = {QUANT["bf16"]: 2.0, QUANT["fp8_tensor"]: 1.0, QUANT["fp8_block"]: 1.0,
+          QUANT["w4a8"]: 0.5, QUANT["mxfp8"]: 1.0, QUANT["mxfp4"]: 0.5}[q]
+    sc = {QUANT["bf16"]: 0, QUANT["fp8_tensor"]: 4,
+          QUANT["fp8_block"]: (n // 128) * (k // 128) * 4, QUANT["w4a8"]: n * (k // 128) * 2,
+          QUANT["mxfp8"]: n * (k // 32), QUANT["mxfp4"]: n * (k // 32)}[q]
+    return int(p.E * n * k * el), int(p.E * sc)
+
+
 def weights(w13, w2, w13_scale=None, w2_scale=None, a1_scale=None, a2_scale=None):
-    return Weights(_ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale), _ptr(a1_scale),
-                   _ptr(a2_scale))
+    """Pointers of packed weights (outputs of moe_pack_w13 / moe_pack_w2)."""
+    a = _Args()
+    ptrs = [a(t, n, 1, None, False) for t, n in ((w13, "w13"), (w2, "w2"),
+                                                   (w13_scale, "w13_scale"),
+                                                   (w2_scale, "w2_scale"),
+                                                   (a1_scale, "a1_scale"),
+                                                   (a2_scale, "a2_scale"))]
+    a.on_gpu()
+    return Weights(*ptrs)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _pack(which, p, src, src_I, src_scale, dst, dst_scale):
+    _check(validate(p), "moe_validate")
+    a = _Args()
+    sb, ssb = _src_bytes(p, which, src_I)
+    db, dsb = packed_bytes(p, which)
+    ptrs = (a(src, "src", sb), a(src_scale, "src_scale", ssb, None, ssb > 0),
+            a(dst, "dst", db), a(dst_scale, "dst_scale", dsb, None, dsb > 0))
+    a.on_gpu()
+    return ptrs
 
 
 def moe_pack_w13(p, src, src_I, swap_halves, src_scale, dst, dst_scale, stream=None):
-    return _check(lib.moe_pack_w13(ctypes.byref(p), _ptr(src), src_I, int(swap_halves),
-                                   _ptr(src_scale), _ptr(dst), _ptr(dst_scale), _stream(stream)),
-                  "moe_pack_w13")
+    s, ss, d, ds = _pack(13, p, src, src_I, src_scale, dst, dst_scale)
+    return _check(lib.moe_pack_w13(ctypes.byref(p), s, src_I, int(swap_halves), ss, d, ds,
+                                   _stream(stream)), "moe_pack_w13")
 
 
 def moe_pack_w2(p, src, src_I, src_scale, dst, dst_scale, stream=None):
-    return _check(lib.moe_pack_w2(ctypes.byref(p), _ptr(src), src_I, _ptr(src_scale), _ptr(dst),
-                                  _ptr(dst_scale), _stream(stream)), "moe_pack_w2")
+    s, ss, d, ds = _pack(2, p, src, src_I, src_scale, dst, dst_scale)
+    return _check(lib.moe_pack_w2(ctypes.byref(p), s, src_I, ss, d, ds, _stream(stream)),
+                  "moe_pack_w2")
 
 
 def moe_route(p, logits, topk_ids, topk_w, stream=None):
-    return _check(lib.moe_route(ctypes.byref(p), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
-                                _stream(stream)), "moe_route")
+    s, a = _shape(p), _Args()
+    lg = a(logits, "logits", s["T"] * s["Er"] * 4, "f32", s["T"] > 0)
+    ids, w = _routing_args(a, s, topk_ids, topk_w, s["T"] > 0)
+    a.on_gpu()
+    return _check(lib.moe_route(ctypes.byref(p), lg, ids, w, _stream(stream)), "moe_route")
 
 
 def moe_align(p, topk_ids, sorted_ids, block_expert, expert_offsets, num_padded, ws,
               stream=None):
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    return _check(lib.moe_align(ctypes.byref(p), _ptr(topk_ids), _ptr(sorted_ids),
-                                _ptr(block_expert), _ptr(expert_offsets), _ptr(num_padded),
-                                _ptr(ws), nbytes, _stream(stream)), "moe_align")
+    s, a = _shape(p), _Args()
+    ids = a(topk_ids, "topk_ids", s["A"] * 4, "i32", s["A"] > 0)
+    al = _align_args(a, s, sorted_ids, block_expert, expert_offsets, num_padded)
+    wsp = a(ws, "ws", 0, None, False)
+    a.on_gpu()
+    return _check(lib.moe_align(ctypes.byref(p), ids, *al, wsp, _nbytes(ws), _stream(stream)),
+                  "moe_align")
 
 
 def moe_prepare(p, logits, topk_ids, topk_w, x, a1_scale, xq, x_scale, sorted_ids,
                 block_expert, expert_offsets, num_padded, ws, stream=None):
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    return _check(lib.moe_prepare(ctypes.byref(p), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
-                                  _ptr(x), _ptr(a1_scale), _ptr(xq), _ptr(x_scale),
-                                  _ptr(sorted_ids), _ptr(block_expert), _ptr(expert_offsets),
-                                  _ptr(num_padded), _ptr(ws), nbytes, _stream(stream)),
-                  "moe_prepare")
+    s, a = _shape(p), _Args()
+    lg = a(logits, "logits", s["T"] * s["Er"] * 4, "f32", False)
+    ids, w = _routing_args(a, s, topk_ids, topk_w, False)
+    if s["A"] > 0 and (ids is None or (logits is not None and w is None)):
+        raise ValueError("topk_ids (and with logits, topk_w) are required")
+    xa = _x_args(a, s, x, a1_scale, xq, x_scale) if x is not None else (None,) * 4
+    al = _align_args(a, s, sorted_ids, block_expert, expert_offsets, num_padded)
+    wsp = a(ws, "ws", 0, None, False)
+    a.on_gpu()
+    return _check(lib.moe_prepare(ctypes.byref(p), lg, ids, w, *xa, *al, wsp, _nbytes(ws),
+                                  _stream(stream)), "moe_prepare")
 
 
 def moe_quant_act(p, x, a1_scale, xq, x_scale, stream=None):
-    return _check(lib.moe_quant_act(ctypes.byref(p), _ptr(x), _ptr(a1_scale), _ptr(xq),
-                                    _ptr(x_scale), _stream(stream)), "moe_quant_act")
+    s, a = _shape(p), _Args()
+    if s["q"] == QUANT["bf16"]:
+        return _check(lib.moe_quant_act(ctypes.byref(p), None, None, None, None,
+                                        _stream(stream)), "moe_quant_act")
+    xa = _x_args(a, s, x, a1_scale, xq, x_scale)
+    a.on_gpu()
+    return _check(lib.moe_quant_act(ctypes.byref(p), *xa, _stream(stream)), "moe_quant_act")
 
 
 def moe_gemm1_act(p, x, x_scale, w, sorted_ids, block_expert, num_padded, a2, a2_scale,
                   stream=None):
-    return _check(lib.moe_gemm1_act(ctypes.byref(p), _ptr(x), _ptr(x_scale), ctypes.byref(w),
-                                    _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
-                                    _ptr(a2), _ptr(a2_scale), _stream(stream)), "moe_gemm1_act")
+    s, a = _shape(p), _Args()
+    real = s["A"] > 0
+    bf = s["q"] == QUANT["bf16"]
+    xp = a(x, "x", s["T"] * s["H"] * (2 if bf else 1), "bf16" if bf else "u8", real)
+    xs = a(x_scale, "x_scale", s["xs"], None, real and s["xs"] > 0)
+    bl = _block_args(a, s, sorted_ids, block_expert, num_padded)
+    a2p = a(a2, "a2", s["rows"] * s["I"] * s["a2_el"], "bf16" if bf else "u8", real)
+    a2sp = a(a2_scale, "a2_scale", s["rows"] * s["a2s_row"], None, real and s["a2s_row"] > 0)
+    a.on_gpu()
+    return _check(lib.moe_gemm1_act(ctypes.byref(p), xp, xs, ctypes.byref(w), *bl, a2p, a2sp,
+                                    _stream(stream)), "moe_gemm1_act")
 
 
 def moe_gemm2_combine(p, a2, a2_scale, w, sorted_ids, block_expert, num_padded, topk_ids,
                       topk_w, y_ws, out, stream=None):
-    nbytes = 0 if y_ws is None else y_ws.numel() * y_ws.element_size()
-    return _check(lib.moe_gemm2_combine(ctypes.byref(p), _ptr(a2), _ptr(a2_scale),
-                                        ctypes.byref(w), _ptr(sorted_ids), _ptr(block_expert),
-                                        _ptr(num_padded), _ptr(topk_ids), _ptr(topk_w),
-                                        _ptr(y_ws), nbytes, _ptr(out), _stream(stream)),
+    s, a = _shape(p), _Args()
+    real = s["T"] > 0
+    bf = s["q"] == QUANT["bf16"]
+    a2p = a(a2, "a2", s["rows"] * s["I"] * s["a2_el"], "bf16" if bf else "u8", real)
+    a2sp = a(a2_scale, "a2_scale", s["rows"] * s["a2s_row"], None, real and s["a2s_row"] > 0)
+    bl = _block_args(a, s, sorted_ids, block_expert, num_padded)
+    ids, wt = _routing_args(a, s, topk_ids, topk_w, real)
+    outp = a(out, "out", s["T"] * s["H"] * 2, "bf16", real)
+    yp = a(y_ws, "y_ws", 0, None, False)
+    a.on_gpu()
+    return _check(lib.moe_gemm2_combine(ctypes.byref(p), a2p, a2sp, ctypes.byref(w), *bl, ids,
+                                        wt, yp, _nbytes(y_ws), outp, _stream(stream)),
                   "moe_gemm2_combine")
 
 
 def moe_forward(p, w, x, logits, topk_ids, topk_w, out, ws, stream=None):
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    return _check(lib.moe_forward(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(logits),
-                                  _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws), nbytes,
-                                  _stream(stream)), "moe_forward")
+    s, a = _shape(p), _Args()
+    real = s["T"] > 0
+    xp = a(x, "x", s["T"] * s["H"] * 2, "bf16", real)
+    lg = a(logits, "logits", s["T"] * s["Er"] * 4, "f32", False)
+    ids, wt = _routing_args(a, s, topk_ids, topk_w, real and logits is None)
+    outp = a(out, "out", s["T"] * s["H"] * 2, "bf16", real)
+    wsp = a(ws, "ws", 0, None, False)
+    a.on_gpu()
+    return _check(lib.moe_forward(ctypes.byref(p), ctypes.byref(w), xp, lg, ids, wt, outp, wsp,
+                                  _nbytes(ws), _stream(stream)), "moe_forward")
 
 
 # ------------------------------------------------------------------ measurement

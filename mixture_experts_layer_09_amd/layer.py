@@ -56,7 +56,14 @@ class MoELayer:
         return self._ws
 
     def forward(self, x, logits=None, topk_ids=None, topk_w=None, out=None):
+        H, K = self.kw["H"], self.kw["top_k"] + self.kw["n_shared"]
+        if x.dim() != 2 or x.shape[1] != H:
+            raise ValueError(f"x must be [T, {H}], got {tuple(x.shape)}")
         T = x.shape[0]
+        for t, name, cols in ((logits, "logits", self.kw["E_routed"]), (topk_ids, "topk_ids", K),
+                              (topk_w, "topk_w", K), (out, "out", H)):
+            if t is not None and tuple(t.shape) != (T, cols):
+                raise ValueError(f"{name} must be [{T}, {cols}], got {tuple(t.shape)}")
         p = self.problem(T)
         if out is None:
             out = torch.empty((T, self.kw["H"]), dtype=torch.bfloat16, device=self.device)
