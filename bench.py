@@ -2,33 +2,40 @@
 """Throughput of the fused MoE layer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload cfg2_M64] [--act A] [--quant Q]
-                    [--gpus 1]
+                    [--gpus 1] [--no-prefill] [--prefill-steps P]
 
 One step is one whole pass of the layer -- route + (fp8 quantise) + align,
 GEMM1 + activation, GEMM2 + combine -- over one batch of synthetic tokens
-already resident in HBM, issued as the C-ABI entry points on the current HIP
-stream (the same sequence moe_forward runs).  The default workload is the
-decode-sized bf16 gated MoE (hidden 2048, 128 experts, top-8, intermediate
-768) at M = 64 tokens.  K steps are timed back to back between two device
-synchronisations; HIP events recorded on the same stream around GEMM1 in each
-timed step give the duration for the roofline of the dominant kernel (GEMM1,
-which streams two thirds of the weight bytes).  A short loop after the timed
-region, with events around every entry point, gives the other calls' share
-(``layer``): each event record costs the stream a few microseconds, so the
-timed passes carry only GEMM1's two.
+already resident in HBM, issued as one moe_forward call through the C ABI on
+the current HIP stream.  The default workload is the decode-sized bf16 gated
+MoE (hidden 2048, 128 experts, top-8, intermediate 768) at M = 64 tokens.  K
+steps are timed back to back between two device synchronisations (wall
+clock; HIP events on the stream at both ends give the GPU's own time).
+
+The dominant kernel (GEMM1, which streams two thirds of the weight bytes) is
+then timed in a second loop of K passes issued as the separate entry points,
+with HIP events recorded on the same stream around GEMM1 only (an event
+record costs the stream about 3 us at decode sizes, so the pass is not cut at
+every kernel boundary); a short loop with events at every call gives the
+other calls' share (``layer``).
 
 Printed: one JSON line.  ``roofline`` relates GEMM1's algorithmic bytes
 (W13 of the experts the batch routes to, the tokens' hidden rows and the
-half-width intermediate it writes) to its measured time and the 8 TB/s HBM
-peak -- or, where its MFMA time at the nominal peaks exceeds its weight
+half-width intermediate it writes) to its event-timed duration and the 8 TB/s
+HBM peak -- or, where its MFMA time at the nominal peaks exceeds its weight
 streaming time (prefill sizes), its algorithmic FLOPs to the dense MFMA peak
-of its dtype; ``measured_peaks`` are the same device's achievable read-stream
-bandwidth and MFMA throughput, measured after the timed region with the
-library's measurement kernels, and ``roofline.frac_of_measured`` relates
-GEMM1 to them; ``cpu_baseline`` is the CPU oracle timed on a bounded sample
-of the same workload on the host cores; ``sweep`` gives every token count of
-the configuration, each pass timed alone after evicting the caches (one
-moe_forward call, and the separate entry points).
+of its dtype; ``roofline.layer`` does the same for the whole pass and the
+step time.  ``prefill`` times, with the default arguments, one moe_forward
+pass per step of the three prefill-sized workloads (fp8 block-scaled with
+the shared expert at M = 4096 -- HBM-bound by its arithmetic intensity --,
+fp8 per-tensor relu^2 and W4A8 at M = 8192) and relates each pass and its
+GEMM1 to the fp8 MFMA peak (or HBM).  ``measured_peaks`` are the same
+device's achievable read-stream bandwidth and MFMA throughput, measured after
+the timed regions with the library's measurement kernels; ``cpu_baseline`` is
+the CPU oracle timed on a bounded sample of the headline workload on the host
+cores; ``sweep`` gives every token count of the headline configuration, each
+pass timed alone after evicting the caches (one moe_forward call, and the
+separate entry points).
 """
 import argparse
 import json
@@ -62,6 +69,10 @@ def parse():
                     help="skip the measured read-stream and MFMA-loop peaks")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill-sized workloads' block")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-workloads", default="cfg3_M4096,cfg4_M8192,cfg5_M8192")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter scaling)")
     return ap.parse_args()
@@ -268,40 +279,117 @@ def main():
     sc = synth.make_act_scales(cfg, tok["x_bits"])
     layer = make_layer(cfg, W, sc["a1"], sc["a2"])
     x, lg = to_dev(tok["x_bits"]), to_dev(tok["logits"])
-    ps = Pass(layer, x, lg, M)
+    out_buf = torch.empty((M, cfg.H), dtype=torch.bfloat16, device="cuda")
+    ids_buf = torch.empty((M, cfg.K_slots), dtype=torch.int32, device="cuda")
+
+    def step():
+        layer.forward(x, lg, topk_ids=ids_buf, out=out_buf)
 
     for _ in range(args.warmup):
-        ps.run()
+        step()
     torch.cuda.synchronize()
-    # The timed region: K passes with HIP events around GEMM1 only (an event
-    # record costs the stream about 3 us at these sizes, so the pass is not
-    # cut at every kernel boundary).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # The timed region: K passes, one moe_forward call each, between two
+    # synchronisations; events on the stream at both ends only.
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        ps.run(g1_ev=evs[k])
+    r0.record()
+    for _ in range(args.steps):
+        step()
+    r1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    g1 = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3         # us
-    # GPU time per pass: GEMM1 start to GEMM1 start across the timed passes
-    gpu_ms = (evs[0][0].elapsed_time(evs[-1][0]) / (args.steps - 1) if args.steps > 1
-              else evs[0][0].elapsed_time(evs[0][1]))
     ms = wall * 1e3 / args.steps
-    # the other calls' share, from a short loop with events at every call
-    # after the timed region
-    nb = min(args.steps, 20)
-    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
-    for k in range(nb):
+    gpu_ms = r0.elapsed_time(r1) / args.steps
+
+    # The dominant kernel: K passes as the separate entry points, events
+    # around GEMM1 only; then the other calls' share from a short loop with
+    # events at every call.
+    ps = Pass(layer, x, lg, M)
+    g1 = gemm1_us(ps, args.steps)
+    pre, g2 = breakdown(ps, min(args.steps, 20))
+
+    ids = ids_buf.cpu().numpy()
+    alg = algorithmic(cfg, M, ids)
+    roof, mfma_bound, achieved, mdt = roofline(cfg, alg, g1, key)
+    roof["layer"] = layer_roofline(cfg, alg, ms)
+    out = {
+        "metric": METRIC,
+        "value": round(M / (ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE.get(cfg.quant, "fp8"),
+        "data": "synthetic",
+        "config": {"workload": workload_text(cfg, M), "tokens": M, "global_batch": M,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer": {"gpu_ms_per_step": round(gpu_ms, 4), "us_route_align_quant": round(float(pre), 2),
+                  "us_gemm1": round(float(g1), 2), "us_gemm2_combine": round(float(g2), 2),
+                  "algorithmic_bytes": int(alg["layer_bytes"]),
+                  "hbm_frac": round(alg["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 3),
+                  "touched_experts": alg["touched"], "assignments": alg["assignments"]},
+    }
+    del ps
+    if not args.no_prefill and args.workload == "cfg2_M64" and args.act is None \
+            and args.quant is None:
+        out["prefill"] = prefill_block(args)
+    if not args.no_peaks:
+        pk = measured_peaks()
+        out["measured_peaks"] = pk
+        mp = pk[f"{mdt}_mfma_tflops"] if mfma_bound else pk["hbm_read_gbs"]
+        out["roofline"]["measured_peak"] = mp
+        out["roofline"]["frac_of_measured"] = round(achieved / mp, 4)
+    if not args.no_sweep:
+        out["sweep"] = sweep(cfg, W, layer)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, W, tok, sc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+DTYPE = {"bf16": "bf16", "w4a8": "int4xfp8", "mxfp8": "mxfp8", "mxfp4": "mxfp4xmxfp8"}
+
+
+def workload_text(cfg, M):
+    return (f"{cfg.name} M={M}: hidden {cfg.H}, {cfg.E_routed} routed + {cfg.n_shared} shared "
+            f"experts, top-{cfg.top_k}, intermediate {cfg.I}, {cfg.act}, {cfg.quant}")
+
+
+def gemm1_us(ps, n):
+    """Average GEMM1 duration (us) over n passes of the separate entry points,
+    from HIP events recorded on the launching stream around GEMM1 only."""
+    import numpy as np
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        ps.run(g1_ev=evs[k])
+    torch.cuda.synchronize()
+    return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
+
+
+def breakdown(ps, n):
+    """Average (route + align + quantise, GEMM2 + combine) durations in us."""
+    import numpy as np
+    import torch
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    for k in range(n):
         ps.run(evb[k])
     torch.cuda.synchronize()
     pre = np.mean([e[0].elapsed_time(e[1]) for e in evb]) * 1e3
     g2 = np.mean([e[2].elapsed_time(e[3]) for e in evb]) * 1e3
+    return float(pre), float(g2)
 
-    ids = ps.b["topk_ids"].cpu().numpy()
-    alg = algorithmic(cfg, M, ids)
-    # GEMM1's bound: the larger of its weight-streaming and its MFMA time at
-    # the nominal peaks
+
+def roofline(cfg, alg, g1, key):
+    """GEMM1's roofline: the larger of its weight-streaming and its MFMA time at
+    the nominal peaks decides the bound."""
     mdt = "bf16" if cfg.quant == "bf16" else "fp8"
     mpeak = MFMA_PEAK_TFLOPS[mdt]
     mfma_bound = alg["gemm1_flops"] / (mpeak * 1e12) > alg["gemm1_bytes"] / (HBM_PEAK_GBS * 1e9)
@@ -319,43 +407,69 @@ def main():
                 "traffic": traffic_record(key),
                 "algorithmic_bytes_per_launch": int(alg["gemm1_bytes"]),
                 "avg_launch_us": round(float(g1), 2)}
-    out = {
-        "metric": METRIC,
-        "value": round(M / (ms * 1e-3), 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "w4a8": "int4xfp8", "mxfp8": "mxfp8",
-                  "mxfp4": "mxfp4xmxfp8"}.get(cfg.quant, "fp8"),
-        "data": "synthetic",
-        "config": {"workload": f"{cfg.name} M={M}: hidden {cfg.H}, {cfg.E_routed} routed "
-                               f"+ {cfg.n_shared} shared experts, top-{cfg.top_k}, "
-                               f"intermediate {cfg.I}, {cfg.act}, {cfg.quant}",
-                   "tokens": M, "global_batch": M, "parallelism": "none (1 GPU)"},
-        "roofline": roof,
-        "layer": {"gpu_ms_per_step": round(gpu_ms, 4), "us_route_align_quant": round(float(pre), 2),
-                  "us_gemm1": round(float(g1), 2), "us_gemm2_combine": round(float(g2), 2),
-                  "algorithmic_bytes": int(alg["layer_bytes"]),
-                  "hbm_frac": round(alg["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                  "tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 3),
-                  "touched_experts": alg["touched"], "assignments": alg["assignments"]},
-    }
-    if not args.no_peaks:
-        pk = measured_peaks()
-        out["measured_peaks"] = pk
-        mp = pk[f"{mdt}_mfma_tflops"] if mfma_bound else pk["hbm_read_gbs"]
-        out["roofline"]["measured_peak"] = mp
-        out["roofline"]["frac_of_measured"] = round(achieved / mp, 4)
-    if not args.no_sweep:
-        out["sweep"] = sweep(cfg, W, layer)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, W, tok, sc, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    return roof, mfma_bound, achieved, mdt
+
+
+def layer_roofline(cfg, alg, ms):
+    """The whole pass against its binding roofline (by arithmetic intensity)."""
+    mdt = "bf16" if cfg.quant == "bf16" else "fp8"
+    mpeak = MFMA_PEAK_TFLOPS[mdt]
+    t = ms * 1e-3
+    if alg["flops"] / (mpeak * 1e12) > alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9):
+        a = alg["flops"] / t / 1e12
+        return {"bound": "mfma", "achieved": round(a, 1), "peak": mpeak, "unit": "TFLOP/s",
+                "frac": round(a / mpeak, 4), "algorithmic_flops": int(alg["flops"]),
+                "ms_per_pass": round(ms, 4)}
+    a = alg["layer_bytes"] / t / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(alg["layer_bytes"]),
+            "ms_per_pass": round(ms, 4)}
+
+
+def prefill_block(args):
+    """One moe_forward pass per step of each prefill-sized workload: tokens/s,
+    TFLOP/s and the pass's and GEMM1's fractions of their roofline."""
+    import torch
+    import synth
+    res = []
+    for name in args.prefill_workloads.split(","):
+        cfg, M = workload(name)
+        t_gen = time.perf_counter()
+        W = synth.make_weights(cfg)
+        tok = synth.make_tokens(cfg, M)
+        sc = synth.make_act_scales(cfg, tok["x_bits"])
+        layer = make_layer(cfg, W, sc["a1"], sc["a2"])
+        del W
+        x, lg = to_dev(tok["x_bits"]), to_dev(tok["logits"])
+        out = torch.empty((M, cfg.H), dtype=torch.bfloat16, device="cuda")
+        ids = torch.empty((M, cfg.K_slots), dtype=torch.int32, device="cuda")
+        gen_s = time.perf_counter() - t_gen
+        for _ in range(2):
+            layer.forward(x, lg, topk_ids=ids, out=out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.prefill_steps):
+            layer.forward(x, lg, topk_ids=ids, out=out)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.prefill_steps
+        ps = Pass(layer, x, lg, M)
+        g1 = gemm1_us(ps, 5)
+        pre, g2 = breakdown(ps, 5)
+        alg = algorithmic(cfg, M, ids.cpu().numpy())
+        roof, _, _, _ = roofline(cfg, alg, g1, name)
+        lay = layer_roofline(cfg, alg, ms)
+        res.append({"workload": workload_text(cfg, M), "key": name, "tokens": M,
+                    "ms_per_step": round(ms, 4), "tokens_per_s": round(M / (ms * 1e-3), 1),
+                    "tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 1),
+                    "dtype": DTYPE.get(cfg.quant, "fp8"), "layer": lay,
+                    "gemm1": {"us": round(g1, 1), "bound": roof["bound"], "frac": roof["frac"],
+                              "achieved": roof["achieved"], "unit": roof["unit"]},
+                    "us_route_align_quant": round(pre, 1), "us_gemm2_combine": round(g2, 1),
+                    "setup_s": round(gen_s, 1)})
+        print(f"prefill {name}: {ms:.3f} ms/pass", file=sys.stderr, flush=True)
+        del layer, ps, x, lg, out, ids
+        torch.cuda.empty_cache()
+    return res
 
 
 def measured_peaks():
