@@ -330,6 +330,32 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const uint16_t* x,
                 const float* logits, int32_t* topk_ids, float* topk_w,
                 uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* Bytes of the library's fixed per-GPU workspace used by moe_forward_noalloc. */
+#define MOE_NOALLOC_WORKSPACE_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate device memory -- code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc: the same kernels and results as moe_forward (bit-identical
+ * output), with the workspace taken from a fixed array of
+ * MOE_NOALLOC_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  It allocates nothing, calls no allocating routine
+ * and leaves no state that a later call depends on (every value the kernels
+ * read back is written earlier in the same call, so nothing must start at
+ * zero).
+ *   Arguments as moe_forward, without ws / ws_bytes.  `stream` must belong
+ *   to the current device (NULL: the null stream of the current device).
+ *   The first call on a device looks up the array's device address
+ *   (hipGetSymbolAddress); make that call outside stream capture.
+ * Returns MOE_ERR_WORKSPACE, before anything is enqueued, when
+ * moe_workspace_bytes(p) exceeds MOE_NOALLOC_WORKSPACE_BYTES (decode-sized
+ * batches fit: e.g. hidden 2048, 128 experts, top-8, intermediate 768 up to
+ * several hundred tokens).  Every call on a GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams or threads) race
+ * and must be serialised by the caller. */
+int moe_forward_noalloc(const moe_problem* p, const moe_weights* w, const uint16_t* x,
+                        const float* logits, int32_t* topk_ids, float* topk_w,
+                        uint16_t* out, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,8 +26,11 @@ EXPORTS = (
     "moe_block_m", "moe_max_blocks", "moe_max_padded_rows", "moe_align_workspace_bytes",
     "moe_combine_workspace_bytes", "moe_workspace_bytes", "moe_packed_bytes",
     "moe_pack_w13", "moe_pack_w2", "moe_route", "moe_align", "moe_prepare", "moe_quant_act",
-    "moe_gemm1_act", "moe_gemm2_combine", "moe_forward",
+    "moe_gemm1_act", "moe_gemm2_combine", "moe_forward", "moe_forward_noalloc",
 )
+# bytes of the fixed per-GPU workspace of moe_forward_noalloc
+# (MOE_NOALLOC_WORKSPACE_BYTES in include/moe.h)
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 HOST_ONLY = EXPORTS[:11]
 # measurement helpers declared in include/moe_probe.h (not part of the layer)
 PROBE_EXPORTS = ("moe_probe_read", "moe_probe_read_blocks", "moe_probe_mfma",
@@ -88,6 +91,8 @@ def _declare(lib, host_only=False):
                                              _VP, _VP, _VP, _VP, _SZ, _VP, _VP]),
         "moe_forward": (ctypes.c_int, [_P, ctypes.POINTER(Weights), _VP, _VP, _VP, _VP, _VP,
                                        _VP, _SZ, _VP]),
+        "moe_forward_noalloc": (ctypes.c_int, [_P, ctypes.POINTER(Weights), _VP, _VP, _VP, _VP,
+                                               _VP, _VP]),
         "moe_probe_read": (ctypes.c_int, [_VP, _SZ, _VP, _VP]),
         "moe_probe_read_blocks": (_I32, []),
         "moe_probe_mfma": (ctypes.c_int, [_I32, _I32, _VP, _VP]),
@@ -437,6 +442,19 @@ def moe_forward(p, w, x, logits, topk_ids, topk_w, out, ws, stream=None):
     a.on_gpu()
     return _check(lib.moe_forward(ctypes.byref(p), ctypes.byref(w), xp, lg, ids, wt, outp, wsp,
                                   _nbytes(ws), _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(p, w, x, logits, topk_ids, topk_w, out, stream=None):
+    """moe_forward with the library's fixed per-GPU workspace (no allocation)."""
+    s, a = _shape(p), _Args()
+    real = s["T"] > 0
+    xp = a(x, "x", s["T"] * s["H"] * 2, "bf16", real)
+    lg = a(logits, "logits", s["T"] * s["Er"] * 4, "f32", False)
+    ids, wt = _routing_args(a, s, topk_ids, topk_w, real and logits is None)
+    outp = a(out, "out", s["T"] * s["H"] * 2, "bf16", real)
+    a.on_gpu()
+    return _check(lib.moe_forward_noalloc(ctypes.byref(p), ctypes.byref(w), xp, lg, ids, wt,
+                                          outp, _stream(stream)), "moe_forward_noalloc")
 
 
 # ------------------------------------------------------------------ measurement

@@ -197,3 +197,27 @@ def test_import_fails_without_the_library(tmp_path):
                        cwd=tmp_path, capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libmoe.so is missing" in r.stderr
+
+
+def test_noalloc_capacity_and_rejection():
+    """moe_forward_noalloc's fixed workspace: the header's size matches the
+    binding's, and a problem needing more is refused with MOE_ERR_WORKSPACE
+    before anything touches a device (the pointers are never dereferenced)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.NOALLOC_WORKSPACE_BYTES
+    big = P(T=4096, H=2048, I=768, E_routed=128, top_k=8)
+    assert moe.lib.moe_workspace_bytes(ctypes.byref(big)) > moe.NOALLOC_WORKSPACE_BYTES
+    dummy = ctypes.c_void_p(16)
+    w = moe.Weights()
+    st = moe.lib.moe_forward_noalloc(ctypes.byref(big), ctypes.byref(w), dummy, dummy, None,
+                                     None, dummy, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    assert b"moe_forward_noalloc holds" in moe.lib.moe_last_error()
+    # the decode-sized workloads fit
+    for kw in (dict(T=64, H=2048, I=768, E_routed=128, top_k=8),
+               dict(T=16, H=2048, I=512, E_routed=512, top_k=10, n_shared=1, quant="fp8_block"),
+               dict(T=128, H=4096, I=2688, E_routed=128, top_k=6, act="relu2",
+                    quant="fp8_tensor")):
+        p = P(**kw)
+        assert moe.lib.moe_workspace_bytes(ctypes.byref(p)) <= moe.NOALLOC_WORKSPACE_BYTES
