@@ -34,7 +34,7 @@ NOALLOC_WORKSPACE_BYTES = 64 << 20
 HOST_ONLY = EXPORTS[:11]
 # measurement helpers declared in include/moe_probe.h (not part of the layer)
 PROBE_EXPORTS = ("moe_probe_read", "moe_probe_read_blocks", "moe_probe_mfma",
-                 "moe_probe_mfma_blocks", "moe_probe_mfma_flops")
+                 "moe_probe_mfma_blocks", "moe_probe_mfma_flops", "moe_probe_mfma_tile")
 
 
 class MoEError(RuntimeError):
@@ -98,6 +98,7 @@ def _declare(lib, host_only=False):
         "moe_probe_mfma": (ctypes.c_int, [_I32, _I32, _VP, _VP]),
         "moe_probe_mfma_blocks": (_I32, []),
         "moe_probe_mfma_flops": (_I64, [_I32, _I32]),
+        "moe_probe_mfma_tile": (ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     }
     for name in (HOST_ONLY if host_only else EXPORTS + PROBE_EXPORTS):
         fn = getattr(lib, name)
@@ -469,3 +470,16 @@ def probe_mfma(dtype, iters, sink, stream=None):
     d = {"bf16": 0, "fp8": 1}[dtype]
     _check(lib.moe_probe_mfma(d, iters, _ptr(sink), _stream(stream)), "moe_probe_mfma")
     return lib.moe_probe_mfma_flops(d, iters)
+
+
+def probe_mfma_tile(fmt, a, b, c, d, sa=None, sb=None, stream=None):
+    """One matrix-core instruction on one wave (include/moe_probe.h):
+    fmt "bf16" (a, b: int16 [64, 8]) or "fp8" (a, b: uint8 [64, 32]); c, d:
+    float32 [64, 4]; sa, sb: uint8 [64] E8M0 codes or None."""
+    f = {"bf16": 0, "fp8": 1}[fmt]
+    per = 16 if f == 0 else 32
+    g = _Args()
+    ptrs = (g(a, "a", 64 * per), g(b, "b", 64 * per), g(sa, "sa", 64, None, False),
+            g(sb, "sb", 64, None, False), g(c, "c", 64 * 16, "f32"), g(d, "d", 64 * 16, "f32"))
+    g.on_gpu()
+    return _check(lib.moe_probe_mfma_tile(f, *ptrs, _stream(stream)), "moe_probe_mfma_tile")

@@ -12,6 +12,7 @@
 
 #include "../../include/moe_probe.h"
 #include "moe_device.hpp"
+#include "moe_gemm_common.hpp"
 #include "moe_plan.hpp"
 
 namespace moe {
@@ -81,6 +82,32 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __res
   sink[size_t(blockIdx.x) * blockDim.x + threadIdx.x] = s;
 }
 
+// One matrix-core instruction on one wave: D = A.B + C on a 16 x 16 tile
+// with the lane layouts of include/moe_probe.h (fmt 0 bf16, fmt 1 e4m3 with
+// the E8M0 scale codes of each lane).
+template <int FMT>
+__global__ __launch_bounds__(64) void probe_mfma_tile_kernel(const uint8_t* __restrict__ a,
+                                                             const uint8_t* __restrict__ b,
+                                                             const uint8_t* __restrict__ sa,
+                                                             const uint8_t* __restrict__ sb,
+                                                             const float* __restrict__ c,
+                                                             float* __restrict__ d) {
+  const int l = threadIdx.x;
+  const f32x4 cc = *reinterpret_cast<const f32x4*>(c + l * 4);
+  f32x4 r;
+  if constexpr (FMT == 0) {
+    const u32x4 av = *reinterpret_cast<const u32x4*>(a + l * 16);
+    const u32x4 bv = *reinterpret_cast<const u32x4*>(b + l * 16);
+    r = mfma_bf16(av, bv, cc);
+  } else {
+    const u32x4* ap = reinterpret_cast<const u32x4*>(a + l * 32);
+    const u32x4* bp = reinterpret_cast<const u32x4*>(b + l * 32);
+    const int sav = sa ? int(sa[l]) : 127, sbv = sb ? int(sb[l]) : 127;
+    r = mfma_mx<0, 0>(fp8_pair(ap[0], ap[1]), fp8_pair(bp[0], bp[1]), cc, sav, sbv);
+  }
+  *reinterpret_cast<f32x4*>(d + l * 4) = r;
+}
+
 int cu_count() {
   static std::atomic<int> cus[64];
   int dev = 0;
@@ -131,6 +158,24 @@ int moe_probe_mfma(int32_t dtype, int32_t iters, float* sink, moe_stream_t strea
   else moe::probe_mfma_kernel<0><<<grid, block, 0, (hipStream_t)stream>>>(iters, sink);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return moe::fail(MOE_ERR_HIP, std::string("moe_probe_mfma: ") + hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int moe_probe_mfma_tile(int32_t fmt, const void* a, const void* b, const uint8_t* sa,
+                        const uint8_t* sb, const float* c, float* d, moe_stream_t stream) {
+  moe::clear_error();
+  if ((fmt != 0 && fmt != 1) || !a || !b || !c || !d)
+    return moe::fail(MOE_ERR_INVALID_ARG, "moe_probe_mfma_tile: fmt 0 or 1, a, b, c, d");
+  (void)hipGetLastError();
+  const auto* ab = static_cast<const uint8_t*>(a);
+  const auto* bb = static_cast<const uint8_t*>(b);
+  if (fmt == 0)
+    moe::probe_mfma_tile_kernel<0><<<1, 64, 0, (hipStream_t)stream>>>(ab, bb, sa, sb, c, d);
+  else
+    moe::probe_mfma_tile_kernel<1><<<1, 64, 0, (hipStream_t)stream>>>(ab, bb, sa, sb, c, d);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return moe::fail(MOE_ERR_HIP, std::string("moe_probe_mfma_tile: ") + hipGetErrorString(e));
   return MOE_OK;
 }
 

@@ -37,6 +37,9 @@ from .moe import (  # noqa: F401
     dequant_w13,
     dequant_w2,
     store_intermediate,
-    flip_margin,
+    intermediate_window,
+    gemm1_window,
+    mfma_dot_model,
+    activation_window,
     moe_forward,
 )
