@@ -311,7 +311,10 @@ int moe_gemm1_act(const moe_problem* p, const void* x, const void* x_scale,
  *   out[t]  = bf16( sum over j with 0 <= topk_ids[t][j] < E of y_{t*K'+j} ),
  *             summed in slot order j = 0..K'-1, rounded once
  * out is written completely (rows with no valid slot become 0).
- *   y_ws   : moe_combine_workspace_bytes(p) bytes of scratch. */
+ *   y_ws   : moe_combine_workspace_bytes(p) bytes of scratch (not touched when
+ *            the block is 16 rows and T*K' <= 64: GEMM2 and the sum then run
+ *            token by token in one kernel, with the same arithmetic and
+ *            bit-identical output). */
 int moe_gemm2_combine(const moe_problem* p, const void* a2, const void* a2_scale,
                       const moe_weights* w, const int32_t* sorted_ids,
                       const int32_t* block_expert, const int32_t* num_padded,

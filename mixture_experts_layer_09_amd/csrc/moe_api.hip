@@ -242,6 +242,10 @@ int moe_gemm2_combine(const moe_problem* p, const void* a2, const void* a2_scale
   float* y = static_cast<float*>(y_ws);
   hipStream_t s = (hipStream_t)stream;
   clear_stale_launch_error();
+  if (q.g2_tok)
+    return hip_status(moe::launch_gemm2_combine_tok(*p, q, a2, a2_scale, *w, sorted_ids,
+                                                    num_padded, topk_ids, topk_w, out, s),
+                      "moe_gemm2_combine");
   st = hip_status(moe::launch_gemm2(*p, q, a2, a2_scale, *w, sorted_ids, block_expert,
                                     num_padded, topk_w, y, s),
                   "moe_gemm2_combine (gemm)");
@@ -294,6 +298,10 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const uint16_t* x,
   if ((st = hip_status(moe::launch_gemm1(*p, q, xin, xs, *w, sorted, bexp, npad, a2, a2s, s),
                        "gemm1")) != MOE_OK)
     return st;
+  if (q.g2_tok)
+    return hip_status(moe::launch_gemm2_combine_tok(*p, q, a2, a2s, *w, sorted, npad, ids, wts,
+                                                    out, s),
+                      "gemm2+combine");
   if ((st = hip_status(moe::launch_gemm2(*p, q, a2, a2s, *w, sorted, bexp, npad, wts, y, s),
                        "gemm2")) != MOE_OK)
     return st;

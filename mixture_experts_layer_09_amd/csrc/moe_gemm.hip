@@ -338,6 +338,182 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   *reinterpret_cast<u32x4*>(out + size_t(t) * H + c) = o;
 }
 
+// GEMM2 and the combine in one kernel, token by token, for small batches: a
+// workgroup owns one token and 16 output channels and runs GEMM2 for each of
+// the token's slots -- the same fragments, k ranges and four-way K split as
+// gemm_stream<2, Q, 0, WT, 4>, so every slot's fp32 row is the one that
+// kernel writes -- then sums the routing-weighted rows in slot order and
+// rounds once to bf16, as combine_kernel does: the output is bit-identical to
+// gemm_stream<2> followed by combine_kernel, without the per-assignment rows
+// leaving the chip.  16 waves: wave w takes K quarter w % 4 of the slots
+// (w / 4), (w / 4) + 4, ..., so that a wave has all its k-steps in flight at
+// once.  The padded row of each slot's intermediate is found by a scan of
+// sorted_ids.  Each weight tile a token routes to is streamed for that token
+// alone, which is what a batch of a handful of tokens does anyway.
+template <int Q>
+__global__ __launch_bounds__(1024) void gemm2_combine_tok(GemmArgs g, const int32_t* __restrict__ ids,
+                                                         uint16_t* __restrict__ out, int E) {
+  using T = QT<Q>;
+  constexpr int KS = 4, SG = 4;                       // K quarters x slot groups = 16 waves
+  constexpr int D = Q == MOE_QUANT_BF16 ? 8 : 4;      // (slot, k-step) items in flight per wave
+  constexpr bool MX = kMx<Q>;
+  constexpr int BRUN = MX ? 16 : T::KSTEP / 4, BHALF = MX ? kMxHalfStride : 16;
+  constexpr int KMAX = kMaxSlots;
+  __shared__ int slot_row[KS * SG * KMAX];  // per wave: padded row of each slot
+  __shared__ float slot_wgt[KMAX];
+  __shared__ f32x4 red[KS][KMAX][4];  // the 4 lanes holding column 0, per K quarter and slot
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4;
+  const int kq = wave % KS, sg = wave / KS;
+  const int tile = blockIdx.x, t = blockIdx.y, Kp = g.Kp, f0 = t * Kp;
+  // ---- the token's slots, in every wave: lane j holds slot j's expert; the
+  // valid slots (ids in [0, E)) in slot order are the set bits of `vmask`
+  const int my_e = lane < Kp ? ids[f0 + lane] : -1;
+  const uint64_t vmask = __ballot(my_e >= 0 && my_e < E);
+  const int nv = __popcll(vmask);
+  // the j-th valid slot: the position of the j-th set bit
+  auto nth_slot = [&](int q) {
+    uint64_t m = vmask;
+    for (int c = 0; c < q; ++c) m &= m - 1;
+    return int(__builtin_ctzll(m));
+  };
+  // the padded row of each slot's intermediate, from a scan of sorted_ids by
+  // this wave (into this wave's part of slot_row: no barrier needed)
+  const int npad = *g.num_padded;
+  int* rows = slot_row + wave * KMAX;
+  for (int r0 = 0; r0 < npad; r0 += 64) {
+    const int r = r0 + lane;
+    const int f = r < npad ? g.sorted_ids[r] : g.A;
+    if (f >= f0 && f < f0 + Kp) rows[f - f0] = r;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes done (lgkmcnt 0)
+  __builtin_amdgcn_wave_barrier();
+  if (wave == 0 && lane < Kp) slot_wgt[lane] = g.topk_w[f0 + lane];
+
+  const int per = (g.steps + KS - 1) / KS;
+  const int s0 = min(g.steps, kq * per), s1 = min(g.steps, s0 + per);
+  const int nsw = s1 - s0;                          // k-steps of this wave per slot
+  const int nmine = nv > sg ? (nv - sg + SG - 1) / SG : 0;  // slots of this wave
+  const int n = nmine * nsw;                        // (slot, k-step) items, slot-major
+  const size_t ebytes = size_t(g.tiles) * g.steps * T::FRAG;
+  const int kblocks = g.K / 128;
+  // this wave's slots in registers, lane q holding its q-th: slot, expert,
+  // padded row (read back per item with a scalar readlane)
+  const int q_slot = lane < nmine ? nth_slot(sg + SG * lane) : 0;
+  const int q_exp = __shfl(my_e, q_slot, 64);
+  const int q_row = lane < nmine ? rows[q_slot] : 0;
+
+  struct Item {
+    u32x4 a[T::AV];
+    u32x4 b[T::BV];
+    float bs, ws;
+    f32x4 ws4;
+    int bsc, wsc4;
+  };
+  auto load = [&](Item& it, int i) {
+    const int qi = i / nsw, s = s0 + i % nsw;
+    const int e = __builtin_amdgcn_readlane(q_exp, qi), m = __builtin_amdgcn_readlane(q_row, qi);
+    const uint8_t* wp = g.w + size_t(e) * ebytes + (size_t(tile) * g.steps + s) * T::FRAG +
+                        lane * 16;
+#pragma unroll
+    for (int v = 0; v < T::AV; ++v) it.a[v] = ld16_stream(wp + v * 1024);
+    const uint8_t* bp = g.b + (size_t(m) * g.K + grp * BRUN) * T::EB + size_t(s) * T::KSTEP * T::EB;
+#pragma unroll
+    for (int v = 0; v < T::BV; ++v) it.b[v] = ld16(bp + v * BHALF);
+    if (Q == MOE_QUANT_FP8_BLOCK) {
+      it.bs = g.b_scale[size_t(m) * kblocks + s];
+      it.ws = g.w_scale[(size_t(e) * (g.N / 128) + tile / 8) * kblocks + s];
+    }
+    if (Q == MOE_QUANT_W4A8)
+      it.ws4 = *reinterpret_cast<const f32x4*>(
+          g.w_scale + ((size_t(e) * g.tiles + tile) * g.steps + s) * 16 + grp * 4);
+    if (MX) {
+      it.bsc = g.b_sc8[size_t(m) * (g.K / 32) + s * 4 + grp];
+      it.wsc4 = *reinterpret_cast<const int*>(
+          g.w_sc8 + (((size_t(e) * (g.tiles / 4) + tile / 4) * g.steps + s) * 64 + lane) * 4);
+    }
+  };
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Item& it) {
+    if (Q == MOE_QUANT_BF16) {
+      acc = mfma_bf16(it.a[0], it.b[0], acc);
+    } else if (MX) {
+      const i32x8 bb = fp8_pair(it.b[0], it.b[1]);
+      acc = mfma_mx_sel<kMxWFmt<Q>, 0>(mx_weight_operand<Q>(it.a[0], it.a[T::AV - 1]), bb, acc,
+                                       it.wsc4, tile % 4, it.bsc);
+    } else {
+      const i32x8 bb = fp8_pair(it.b[0], it.b[1]);
+      if (Q == MOE_QUANT_FP8_TENSOR) {
+        acc = mfma_fp8(fp8_pair(it.a[0], it.a[1]), bb, acc);
+      } else if (Q == MOE_QUANT_FP8_BLOCK) {
+        const f32x4 p = mfma_fp8(fp8_pair(it.a[0], it.a[1]), bb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const float sc = it.bs * it.ws;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(p[i], sc, acc[i]);
+      } else {
+        const f32x4 p = mfma_fp8(int4x32_to_e4m3(it.a[0]), bb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(p[i], it.ws4[i], acc[i]);
+      }
+    }
+  };
+  // the item ring: D items in flight; a slot's partial sum goes to the LDS
+  // after its last k-step
+  Item st[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < n) load(st[d], d);
+  for (int i0 = 0; i0 < n; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = i0 + d;
+      if (i < n) {
+        compute(st[d]);
+        if (i + D < n) load(st[d], i + D);
+        if ((i + 1) % nsw == 0) {
+          if ((lane & 15) == 0) red[kq][__builtin_amdgcn_readlane(q_slot, i / nsw)][grp] = acc;
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+  if (nsw == 0)
+    for (int q = 0; q < nmine; ++q) {
+      const int j = __builtin_amdgcn_readlane(q_slot, q);
+      if ((lane & 15) == 0) red[kq][j][grp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  __syncthreads();
+  // ---- K-split partial sums in quarter order, routing weight, slot-order sum
+  // (wave 0; the lanes holding column 0 accumulate, the loop is uniform)
+  if (wave == 0) {
+    const bool col0 = (lane & 15) == 0;
+    float alpha = 1.f;
+    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < nv; ++q) {
+      const int j = nth_slot(q);
+      const int e = __shfl(my_e, j, 64);
+      if (Q == MOE_QUANT_FP8_TENSOR) alpha = g.w_scale[e] * *g.a2;
+      if (Q == MOE_QUANT_W4A8) alpha = *g.a2;
+      const float wgt = alpha * slot_wgt[j];
+      if (col0) {
+        f32x4 a = red[0][j][grp];
+#pragma unroll
+        for (int k = 1; k < KS; ++k) a += red[k][j][grp];
+        // the row value first (as GEMM2 stores it), then the slot-order sum:
+        // kept apart so that no fused multiply-add changes the rounding
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] = __fadd_rn(sum[i], __fmul_rn(a[i], wgt));
+      }
+    }
+    if (col0) {
+      u32x2 o;
+      o[0] = bf16_bits(sum[0]) | (bf16_bits(sum[1]) << 16);
+      o[1] = bf16_bits(sum[2]) | (bf16_bits(sum[3]) << 16);
+      *reinterpret_cast<u32x2*>(out + size_t(t) * g.H + tile * 16 + grp * 4) = o;
+    }
+  }
+}
+
 namespace {
 
 template <int PHASE, int Q, int ACT>
@@ -460,6 +636,57 @@ hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, con
   }
   const dim3 grid = stream_grid(q.g2, a.tiles, q.max_blocks);
   return dispatch_quant<2, 0>(p.quant, q.g2, grid, a, stream);
+}
+
+hipError_t launch_gemm2_combine_tok(const moe_problem& p, const Plan& q, const void* a2,
+                                   const void* a2s, const moe_weights& w,
+                                   const int32_t* sorted_ids, const int32_t* num_padded,
+                                   const int32_t* topk_ids, const float* topk_w, uint16_t* out,
+                                   hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  GemmArgs a{};
+  a.b = static_cast<const uint8_t*>(a2);
+  a.b_scale = static_cast<const float*>(a2s);
+  a.b_sc8 = static_cast<const uint8_t*>(a2s);
+  a.w = static_cast<const uint8_t*>(w.w2);
+  a.w_scale = static_cast<const float*>(w.w2_scale);
+  a.w_sc8 = static_cast<const uint8_t*>(w.w2_scale);
+  a.a1 = w.a1_scale;
+  a.a2 = w.a2_scale;
+  a.sorted_ids = sorted_ids;
+  a.num_padded = num_padded;
+  a.topk_w = topk_w;
+  a.K = p.I;
+  a.N = p.H;
+  a.I = p.I;
+  a.H = p.H;
+  a.Kp = q.Kp;
+  a.A = int(q.A);
+  a.steps = q.ksteps_i;
+  a.tiles = p.H / 16;
+  const dim3 grid(unsigned(a.tiles), unsigned(p.T)), block(1024);
+  switch (p.quant) {
+    case MOE_QUANT_BF16:
+      gemm2_combine_tok<MOE_QUANT_BF16><<<grid, block, 0, stream>>>(a, topk_ids, out, p.E);
+      break;
+    case MOE_QUANT_FP8_TENSOR:
+      gemm2_combine_tok<MOE_QUANT_FP8_TENSOR><<<grid, block, 0, stream>>>(a, topk_ids, out, p.E);
+      break;
+    case MOE_QUANT_FP8_BLOCK:
+      gemm2_combine_tok<MOE_QUANT_FP8_BLOCK><<<grid, block, 0, stream>>>(a, topk_ids, out, p.E);
+      break;
+    case MOE_QUANT_W4A8:
+      gemm2_combine_tok<MOE_QUANT_W4A8><<<grid, block, 0, stream>>>(a, topk_ids, out, p.E);
+      break;
+    case MOE_QUANT_MXFP8:
+      gemm2_combine_tok<MOE_QUANT_MXFP8><<<grid, block, 0, stream>>>(a, topk_ids, out, p.E);
+      break;
+    case MOE_QUANT_MXFP4:
+      gemm2_combine_tok<MOE_QUANT_MXFP4><<<grid, block, 0, stream>>>(a, topk_ids, out, p.E);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const moe_problem& p, const Plan& q, const int32_t* topk_ids,

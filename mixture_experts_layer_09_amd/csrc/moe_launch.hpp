@@ -48,6 +48,14 @@ hipError_t launch_gemm2(const moe_problem& p, const Plan& q, const void* a2, con
                         const int32_t* block_expert, const int32_t* num_padded,
                         const float* topk_w, float* y, hipStream_t stream);
 
+// GEMM2 and the combine in one launch, token by token (Plan::g2_tok):
+// bit-identical to launch_gemm2 followed by launch_combine.
+hipError_t launch_gemm2_combine_tok(const moe_problem& p, const Plan& q, const void* a2,
+                                   const void* a2s, const moe_weights& w,
+                                   const int32_t* sorted_ids, const int32_t* num_padded,
+                                   const int32_t* topk_ids, const float* topk_w, uint16_t* out,
+                                   hipStream_t stream);
+
 hipError_t launch_combine(const moe_problem& p, const Plan& q, const int32_t* topk_ids,
                           const float* y, uint16_t* out, hipStream_t stream);
 

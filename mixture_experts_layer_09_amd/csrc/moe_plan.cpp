@@ -185,6 +185,10 @@ int make_plan(const moe_problem* p, Plan* plan) {
            : p->quant == MOE_QUANT_MXFP4   ? kStreamG1Mxfp4
                                            : kStreamG1;
     q.g2 = kStreamG2;
+    // a handful of tokens: GEMM2 and the combine token by token in one
+    // launch (every weight tile a token routes to is streamed for it alone,
+    // which at this size is what the expert-major kernel does too)
+    q.g2_tok = q.A <= kTokMaxAssign && p->T <= kTokMaxTokens;
   } else {
     // fp8 / int4 / MX weights at 128-row blocks: weights and tokens staged in
     // LDS by direct-to-LDS loads, several k-steps in flight, one persistent

@@ -18,6 +18,8 @@ constexpr int kMaxSlots = 64;      // K' = top_k + n_shared limit (one lane each
 constexpr int kTiledMinRows = 48;  // rows per expert from which the tiled GEMMs run
 constexpr int kMxBlock = 32;       // elements per E8M0 scale in the MX modes
 constexpr int kMaxDim = 1 << 20;   // largest H and I (keeps 2I and padding in int32)
+constexpr int kTokMaxAssign = 64;  // GEMM2 runs token by token up to this many assignments
+constexpr int kTokMaxTokens = 2;   // and tokens (measured: 8 tokens ran slower that way)
 
 // The OCP MX modes (E8M0 scales per 32 K on weights and activations).
 inline bool quant_is_mx(int q) { return q == MOE_QUANT_MXFP8 || q == MOE_QUANT_MXFP4; }
@@ -49,6 +51,7 @@ struct Plan {
   int32_t kstep = 0;       // K elements per MFMA k-step (32 bf16, 128 fp8/int4)
   int32_t a2_elem = 0;     // bytes per intermediate element
   GemmCfg g1{}, g2{};
+  bool g2_tok = false;     // GEMM2 and the combine token by token, in one launch
   // moe_forward workspace layout (byte offsets, 256-B aligned)
   size_t off_ids = 0, off_w = 0, off_sorted = 0, off_bexp = 0, off_offsets = 0,
          off_npad = 0, off_align = 0, off_xq = 0, off_xs = 0, off_a2 = 0,
