@@ -188,7 +188,8 @@ size_t moe_align_workspace_bytes(const moe_problem* p);
 /* Scratch bytes moe_gemm2_combine needs for its per-assignment rows (host). */
 size_t moe_combine_workspace_bytes(const moe_problem* p);
 
-/* Workspace bytes moe_forward needs for the problem (host). */
+/* Workspace bytes moe_forward needs for the problem (host): for more than
+ * 65536 assignments, those of one pass of floor(65536 / K') tokens. */
 size_t moe_workspace_bytes(const moe_problem* p);
 
 /* Bytes of a packed weight (which = 13 for W13, 2 for W2) and of its packed
@@ -312,9 +313,9 @@ int moe_gemm1_act(const moe_problem* p, const void* x, const void* x_scale,
  *             summed in slot order j = 0..K'-1, rounded once
  * out is written completely (rows with no valid slot become 0).
  *   y_ws   : moe_combine_workspace_bytes(p) bytes of scratch (not touched when
- *            the block is 16 rows and T*K' <= 64: GEMM2 and the sum then run
- *            token by token in one kernel, with the same arithmetic and
- *            bit-identical output). */
+ *            the block is 16 rows, T <= 2 and T*K' <= 64: GEMM2 and the sum
+ *            then run token by token in one kernel, with the same arithmetic
+ *            and bit-identical output). */
 int moe_gemm2_combine(const moe_problem* p, const void* a2, const void* a2_scale,
                       const moe_weights* w, const int32_t* sorted_ids,
                       const int32_t* block_expert, const int32_t* num_padded,
@@ -328,7 +329,12 @@ int moe_gemm2_combine(const moe_problem* p, const void* a2, const void* a2_scale
  *              topk_w are the caller's routing (inputs).  With logits given,
  *              topk_ids / topk_w are optional outputs (NULL: kept in ws).
  *   out      : bf16 [T][H].
- *   ws       : moe_workspace_bytes(p) bytes. */
+ *   ws       : moe_workspace_bytes(p) bytes.
+ * A batch of more than 65536 assignments (T*K') runs as consecutive passes
+ * over floor(65536 / K') tokens each, in stream order, every pass a layer
+ * call of its own on the same workspace: the workspace is that of one pass,
+ * so it stops growing with T (each token's output is computed as in a
+ * single pass; only the blocking of the assignments differs). */
 int moe_forward(const moe_problem* p, const moe_weights* w, const uint16_t* x,
                 const float* logits, int32_t* topk_ids, float* topk_w,
                 uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream);

@@ -1,5 +1,6 @@
 // C ABI entry points: validate on the host, then enqueue the kernels.
 // The operation each entry point performs is specified in include/moe.h.
+#include <algorithm>
 #include <string>
 
 #include "moe_launch.hpp"
@@ -53,6 +54,43 @@ int check_weights(const moe_problem& p, const moe_weights* w, int which) {
     if (!w->a2_scale) return null_arg("weights->a2_scale");
   }
   return MOE_OK;
+}
+
+// One layer pass over p.T tokens with plan q (its workspace layout in ws).
+int forward_pass(const moe_problem& p, const moe::Plan& q, const moe_weights& w,
+                 const uint16_t* x, const float* logits, int32_t* topk_ids, float* topk_w,
+                 uint16_t* out, void* ws, hipStream_t s) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(base + q.off_ids);
+  float* wts = topk_w ? topk_w : reinterpret_cast<float*>(base + q.off_w);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + q.off_sorted);
+  int32_t* bexp = reinterpret_cast<int32_t*>(base + q.off_bexp);
+  int32_t* offs = reinterpret_cast<int32_t*>(base + q.off_offsets);
+  int32_t* npad = reinterpret_cast<int32_t*>(base + q.off_npad);
+  int32_t* scratch = reinterpret_cast<int32_t*>(base + q.off_align);
+  uint8_t* xq = base + q.off_xq;
+  void* xs = base + q.off_xs;
+  void* a2 = base + q.off_a2;
+  void* a2s = base + q.off_a2s;
+  float* y = reinterpret_cast<float*>(base + q.off_y);
+  int st;
+  const bool quantise = p.quant != MOE_QUANT_BF16;
+  if ((st = hip_status(moe::launch_prologue(p, q, logits, ids, wts, x, w.a1_scale, xq, xs,
+                                            quantise, sorted, bexp, offs, npad, scratch, s),
+                       "route/align/quantise")) != MOE_OK)
+    return st;
+  const void* xin = quantise ? static_cast<const void*>(xq) : static_cast<const void*>(x);
+  if ((st = hip_status(moe::launch_gemm1(p, q, xin, xs, w, sorted, bexp, npad, a2, a2s, s),
+                       "gemm1")) != MOE_OK)
+    return st;
+  if (q.g2_tok)
+    return hip_status(moe::launch_gemm2_combine_tok(p, q, a2, a2s, w, sorted, npad, ids, wts,
+                                                    out, s),
+                      "gemm2+combine");
+  if ((st = hip_status(moe::launch_gemm2(p, q, a2, a2s, w, sorted, bexp, npad, wts, y, s),
+                       "gemm2")) != MOE_OK)
+    return st;
+  return hip_status(moe::launch_combine(p, q, ids, y, out, s), "combine");
 }
 
 }  // namespace
@@ -273,39 +311,26 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const uint16_t* x,
   } else if (!topk_ids || !topk_w) {
     return moe::fail(MOE_ERR_INVALID_ARG, "without logits, topk_ids and topk_w are required");
   }
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(base + q.off_ids);
-  float* wts = topk_w ? topk_w : reinterpret_cast<float*>(base + q.off_w);
-  int32_t* sorted = reinterpret_cast<int32_t*>(base + q.off_sorted);
-  int32_t* bexp = reinterpret_cast<int32_t*>(base + q.off_bexp);
-  int32_t* offs = reinterpret_cast<int32_t*>(base + q.off_offsets);
-  int32_t* npad = reinterpret_cast<int32_t*>(base + q.off_npad);
-  int32_t* scratch = reinterpret_cast<int32_t*>(base + q.off_align);
-  uint8_t* xq = base + q.off_xq;
-  void* xs = base + q.off_xs;
-  void* a2 = base + q.off_a2;
-  void* a2s = base + q.off_a2s;
-  float* y = reinterpret_cast<float*>(base + q.off_y);
   hipStream_t s = (hipStream_t)stream;
   clear_stale_launch_error();
-
-  const bool quantise = p->quant != MOE_QUANT_BF16;
-  if ((st = hip_status(moe::launch_prologue(*p, q, logits, ids, wts, x, w->a1_scale, xq, xs,
-                                            quantise, sorted, bexp, offs, npad, scratch, s),
-                       "route/align/quantise")) != MOE_OK)
-    return st;
-  const void* xin = quantise ? static_cast<const void*>(xq) : static_cast<const void*>(x);
-  if ((st = hip_status(moe::launch_gemm1(*p, q, xin, xs, *w, sorted, bexp, npad, a2, a2s, s),
-                       "gemm1")) != MOE_OK)
-    return st;
-  if (q.g2_tok)
-    return hip_status(moe::launch_gemm2_combine_tok(*p, q, a2, a2s, *w, sorted, npad, ids, wts,
-                                                    out, s),
-                      "gemm2+combine");
-  if ((st = hip_status(moe::launch_gemm2(*p, q, a2, a2s, *w, sorted, bexp, npad, wts, y, s),
-                       "gemm2")) != MOE_OK)
-    return st;
-  return hip_status(moe::launch_combine(*p, q, ids, y, out, s), "combine");
+  if (q.chunk_T >= p->T)
+    return forward_pass(*p, q, *w, x, logits, topk_ids, topk_w, out, ws, s);
+  // passes over chunk_T tokens each (the stream orders them, so every pass
+  // reuses the one workspace); each pass is a layer call of its own
+  for (int32_t t0 = 0; t0 < p->T; t0 += q.chunk_T) {
+    moe_problem c = *p;
+    c.T = std::min(q.chunk_T, p->T - t0);
+    moe::Plan qc;
+    if ((st = moe::make_plan(&c, &qc)) != MOE_OK) return st;
+    if (qc.ws_total > ws_bytes) return moe::fail(MOE_ERR_WORKSPACE, "workspace too small");
+    const size_t k0 = size_t(t0) * q.Kp;
+    st = forward_pass(c, qc, *w, x + size_t(t0) * p->H,
+                      logits ? logits + size_t(t0) * p->E_routed : nullptr,
+                      topk_ids ? topk_ids + k0 : nullptr, topk_w ? topk_w + k0 : nullptr,
+                      out + size_t(t0) * p->H, ws, s);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

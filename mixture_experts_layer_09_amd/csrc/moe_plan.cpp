@@ -225,6 +225,31 @@ int make_plan(const moe_problem* p, Plan* plan) {
                                                    : 0);
   q.off_y = take(q.combine_ws);
   q.ws_total = o;
+  // moe_forward runs a large batch in passes of at most kChunkAssign
+  // assignments, each with the workspace of its own (smaller) problem, so
+  // that the workspace stops growing with T * K' * H
+  q.chunk_T = p->T;
+  if (q.A > kChunkAssign) {
+    moe_problem c = *p;
+    c.T = int32_t(kChunkAssign / q.Kp);
+    Plan qc;
+    const int st = make_plan(&c, &qc);  // no deeper: qc.A <= kChunkAssign
+    if (st != MOE_OK) return st;
+    q.chunk_T = c.T;
+    q.off_ids = qc.off_ids;
+    q.off_w = qc.off_w;
+    q.off_sorted = qc.off_sorted;
+    q.off_bexp = qc.off_bexp;
+    q.off_offsets = qc.off_offsets;
+    q.off_npad = qc.off_npad;
+    q.off_align = qc.off_align;
+    q.off_xq = qc.off_xq;
+    q.off_xs = qc.off_xs;
+    q.off_a2 = qc.off_a2;
+    q.off_a2s = qc.off_a2s;
+    q.off_y = qc.off_y;
+    q.ws_total = qc.ws_total;
+  }
   *plan = q;
   return MOE_OK;
 }

@@ -20,6 +20,7 @@ constexpr int kMxBlock = 32;       // elements per E8M0 scale in the MX modes
 constexpr int kMaxDim = 1 << 20;   // largest H and I (keeps 2I and padding in int32)
 constexpr int kTokMaxAssign = 64;  // GEMM2 runs token by token up to this many assignments
 constexpr int kTokMaxTokens = 2;   // and tokens (measured: 8 tokens ran slower that way)
+constexpr int64_t kChunkAssign = 65536;  // moe_forward passes over at most this many assignments
 
 // The OCP MX modes (E8M0 scales per 32 K on weights and activations).
 inline bool quant_is_mx(int q) { return q == MOE_QUANT_MXFP8 || q == MOE_QUANT_MXFP4; }
@@ -52,7 +53,9 @@ struct Plan {
   int32_t a2_elem = 0;     // bytes per intermediate element
   GemmCfg g1{}, g2{};
   bool g2_tok = false;     // GEMM2 and the combine token by token, in one launch
-  // moe_forward workspace layout (byte offsets, 256-B aligned)
+  int32_t chunk_T = 0;     // tokens per moe_forward pass (the workspace below is one pass's)
+  // moe_forward workspace layout (byte offsets, 256-B aligned), for a pass of
+  // chunk_T tokens
   size_t off_ids = 0, off_w = 0, off_sorted = 0, off_bexp = 0, off_offsets = 0,
          off_npad = 0, off_align = 0, off_xq = 0, off_xs = 0, off_a2 = 0,
          off_a2s = 0, off_y = 0, ws_total = 0;

@@ -74,21 +74,42 @@ void check_problem(const moe_problem& p) {
   CHECK(q.max_blocks <= q.A);
   CHECK(q.max_rows >= q.A);
   CHECK(moe_workspace_bytes(&p) == q.ws_total);
-  const size_t offs[] = {q.off_ids, q.off_w,  q.off_sorted, q.off_bexp, q.off_offsets, q.off_npad,
-                         q.off_align, q.off_xq, q.off_xs,   q.off_a2,   q.off_a2s,     q.off_y,
-                         q.ws_total};
+  // moe_forward's workspace is that of one pass of chunk_T tokens
+  const int64_t Kp = p.top_k + p.n_shared;
+  moe::Plan w = q;  // the plan of a pass
+  if (q.A <= moe::kChunkAssign) {
+    CHECK(q.chunk_T == p.T);
+  } else {
+    CHECK(q.chunk_T == int32_t(moe::kChunkAssign / Kp));
+    moe_problem c = p;
+    c.T = q.chunk_T;
+    CHECK(moe::make_plan(&c, &w) == MOE_OK);
+    CHECK(w.A <= moe::kChunkAssign);
+    CHECK(w.ws_total == q.ws_total);
+    CHECK(w.off_y == q.off_y && w.off_a2 == q.off_a2 && w.off_sorted == q.off_sorted);
+    // the short last pass fits the same workspace
+    c.T = p.T % q.chunk_T;
+    if (c.T > 0) {
+      moe::Plan t;
+      CHECK(moe::make_plan(&c, &t) == MOE_OK);
+      CHECK(t.ws_total <= q.ws_total);
+    }
+  }
+  const size_t offs[] = {w.off_ids, w.off_w,  w.off_sorted, w.off_bexp, w.off_offsets, w.off_npad,
+                         w.off_align, w.off_xq, w.off_xs,   w.off_a2,   w.off_a2s,     w.off_y,
+                         w.ws_total};
   for (size_t i = 0; i + 1 < sizeof(offs) / sizeof(offs[0]); ++i) {
     CHECK(offs[i] % 256 == 0);
     CHECK(offs[i] < offs[i + 1]);
   }
   // the segments hold what the kernels write into them
-  CHECK(q.off_sorted - q.off_w >= size_t(q.A) * 4);
-  CHECK(q.off_bexp - q.off_sorted >= size_t(q.max_rows) * 4);
-  CHECK(q.off_offsets - q.off_bexp >= size_t(q.max_blocks) * 4);
-  CHECK(q.off_npad - q.off_offsets >= size_t(p.E + 1) * 4);
-  CHECK(q.off_xq - q.off_align >= q.align_ws);
-  CHECK(q.off_a2s - q.off_a2 >= size_t(q.max_rows) * p.I * q.a2_elem);
-  CHECK(q.ws_total - q.off_y >= q.combine_ws);
+  CHECK(w.off_sorted - w.off_w >= size_t(w.A) * 4);
+  CHECK(w.off_bexp - w.off_sorted >= size_t(w.max_rows) * 4);
+  CHECK(w.off_offsets - w.off_bexp >= size_t(w.max_blocks) * 4);
+  CHECK(w.off_npad - w.off_offsets >= size_t(p.E + 1) * 4);
+  CHECK(w.off_xq - w.off_align >= w.align_ws);
+  CHECK(w.off_a2s - w.off_a2 >= size_t(w.max_rows) * p.I * w.a2_elem);
+  CHECK(w.ws_total - w.off_y >= w.combine_ws);
   CHECK(moe_align_workspace_bytes(&p) == q.align_ws);
   CHECK(moe_combine_workspace_bytes(&p) == q.combine_ws);
   size_t w13 = 0, s13 = 0, w2 = 0, s2 = 0;

@@ -221,3 +221,23 @@ def test_noalloc_capacity_and_rejection():
                     quant="fp8_tensor")):
         p = P(**kw)
         assert moe.lib.moe_workspace_bytes(ctypes.byref(p)) <= moe.NOALLOC_WORKSPACE_BYTES
+
+
+def test_workspace_stops_growing_past_one_pass(plan):
+    """moe_forward runs more than 65536 assignments in passes of
+    floor(65536 / K') tokens: its workspace grows with T up to one pass and
+    stays there; the combine's workspace (moe_gemm2_combine takes the whole
+    batch) keeps growing."""
+    ws = lambda **kw: plan.moe_workspace_bytes(ctypes.byref(P(**kw)))
+    cws = lambda **kw: plan.moe_combine_workspace_bytes(ctypes.byref(P(**kw)))
+    for kw, K in ((dict(H=6144, I=1536, E_routed=20, top_k=8, quant="w4a8"), 8),
+                  (dict(H=4096, I=2688, E_routed=128, top_k=6, act="relu2", quant="fp8_tensor"), 6),
+                  (dict(H=2048, I=512, E_routed=512, top_k=10, n_shared=1, quant="fp8_block"), 11)):
+        chunk = 65536 // K
+        one = ws(T=chunk, **kw)
+        assert ws(T=chunk // 2, **kw) < one
+        for T in (chunk + 1, 2 * chunk + 5, 5 * chunk):
+            assert ws(T=T, **kw) == one, (kw, T)
+            assert cws(T=T, **kw) > cws(T=chunk, **kw)
+        # the passes' size is the batch's when it fits in one
+        assert ws(T=chunk, **kw) > ws(T=chunk - 1, **kw)
