@@ -125,7 +125,16 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, bool 
   for (int r = 0; r < top_k; ++r) {
     const uint32_t hv = uint32_t(key[0] >> 32), hj = ~uint32_t(key[0]);
     const uint32_t gv = group_umax<L>(hv);
-    const uint32_t gj = ~group_umax<L>(hv == gv ? ~hj : 0u);  // lowest index at that value
+    // lowest index at that value: with the whole wave as the group and one
+    // lane holding the value (no tie), that lane's index, read directly
+    uint32_t gj;
+    if constexpr (L == 64) {
+      const uint64_t at = __ballot(hv == gv);
+      gj = __popcll(at) == 1 ? uint32_t(__builtin_amdgcn_readlane(int(hj), __builtin_ctzll(at)))
+                             : ~group_umax<L>(hv == gv ? ~hj : 0u);
+    } else {
+      gj = ~group_umax<L>(hv == gv ? ~hj : 0u);
+    }
     const int j = int(gj);
     const float val = float_from_order_bits(gv);
     if (hv == gv && hj == gj) {  // this lane held the pick: drop it
