@@ -192,6 +192,7 @@ struct PrologueArgs {
   int32_t* block_expert;
   int32_t* offsets;
   int32_t* npad;
+  int align;               // 0: routing (and quantisation) only
   const uint16_t* x;       // quantisation (QM != 0)
   const float* a1;
   uint8_t* xq;
@@ -275,9 +276,10 @@ __global__ __launch_bounds__(kThreads) void prologue_small(PrologueArgs a) {
                             a.wts + size_t(tt) * Kp, sids + tt * Kp);
       }
     }
-  } else {
+  } else if (a.align) {
     for (int f = threadIdx.x; f < a.T * Kp; f += kThreads) sids[f] = a.ids_in[f];
   }
+  if (!a.align) return;  // uniform
   __syncthreads();
   align_in_block(sids, a.T * Kp, a.E, a.BM, smem + kThreads, a.sorted_ids, a.block_expert,
                  a.offsets, a.npad);
@@ -539,12 +541,15 @@ hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* log
                            int32_t* ids, float* w, const uint16_t* x, const float* a1,
                            uint8_t* xq, void* xs, bool quantise, int32_t* sorted_ids,
                            int32_t* block_expert, int32_t* offsets, int32_t* num_padded,
-                           int32_t* scratch, hipStream_t stream) {
+                           int32_t* scratch, hipStream_t stream, bool align) {
+  if (!align && !logits && !quantise) return hipSuccess;  // nothing to do
   if (!prologue_fits(p, q)) {
     hipError_t err = hipSuccess;
     if (logits) err = launch_route(p, logits, ids, w, stream);
     if (err != hipSuccess) return err;
-    err = launch_align(p, q, ids, sorted_ids, block_expert, offsets, num_padded, scratch, stream);
+    if (align)
+      err = launch_align(p, q, ids, sorted_ids, block_expert, offsets, num_padded, scratch,
+                         stream);
     if (err != hipSuccess || !quantise) return err;
     return launch_quant_act(p, x, a1, xq, xs, stream);
   }
@@ -566,6 +571,7 @@ hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* log
   a.block_expert = block_expert;
   a.offsets = offsets;
   a.npad = num_padded;
+  a.align = align ? 1 : 0;
   a.x = x;
   a.a1 = a1;
   a.xq = xq;

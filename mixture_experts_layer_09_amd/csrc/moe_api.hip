@@ -75,17 +75,20 @@ int forward_pass(const moe_problem& p, const moe::Plan& q, const moe_weights& w,
   float* y = reinterpret_cast<float*>(base + q.off_y);
   int st;
   const bool quantise = p.quant != MOE_QUANT_BF16;
+  // one token (q.slot_rows): no alignment; GEMM1 takes a block per assignment
   if ((st = hip_status(moe::launch_prologue(p, q, logits, ids, wts, x, w.a1_scale, xq, xs,
-                                            quantise, sorted, bexp, offs, npad, scratch, s),
+                                            quantise, sorted, bexp, offs, npad, scratch, s,
+                                            !q.slot_rows),
                        "route/align/quantise")) != MOE_OK)
     return st;
   const void* xin = quantise ? static_cast<const void*>(xq) : static_cast<const void*>(x);
-  if ((st = hip_status(moe::launch_gemm1(p, q, xin, xs, w, sorted, bexp, npad, a2, a2s, s),
+  if ((st = hip_status(moe::launch_gemm1(p, q, xin, xs, w, sorted, bexp, npad, a2, a2s, s,
+                                         q.slot_rows ? ids : nullptr),
                        "gemm1")) != MOE_OK)
     return st;
   if (q.g2_tok)
     return hip_status(moe::launch_gemm2_combine_tok(p, q, a2, a2s, w, sorted, npad, ids, wts,
-                                                    out, s),
+                                                    out, s, q.slot_rows),
                       "gemm2+combine");
   if ((st = hip_status(moe::launch_gemm2(p, q, a2, a2s, w, sorted, bexp, npad, wts, y, s),
                        "gemm2")) != MOE_OK)

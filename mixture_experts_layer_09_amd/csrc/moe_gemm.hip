@@ -54,13 +54,19 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rg = wave % RG, kp = wave / RG;
   const int blk = blockIdx.y;
-  if (blk * 16 >= *g.num_padded) return;  // uniform: past the last real block
-  const int e = g.block_expert[blk];
+  int e;
+  if (g.slot_ids) {  // block blk: assignment blk alone (a masked slot has no block)
+    e = g.slot_ids[blk];
+    if (e < 0 || e >= g.E) return;  // uniform
+  } else {
+    if (blk * 16 >= *g.num_padded) return;  // uniform: past the last real block
+    e = g.block_expert[blk];
+  }
   const int tile0 = blockIdx.x * TPW + rg * WT;
   const bool active = tile0 < g.tiles;
   const int grp = lane >> 4;            // k-run of the lane
   const int m = blk * 16 + (lane & 15); // padded row = B column of the lane
-  const int f = g.sorted_ids[m];
+  const int f = g.slot_ids ? ((lane & 15) == 0 ? blk : g.A) : g.sorted_ids[m];
 
   // B row of the lane: GEMM1 gathers the token, GEMM2 reads the padded row.
   int brow;
@@ -378,13 +384,18 @@ __global__ __launch_bounds__(1024) void gemm2_combine_tok(GemmArgs g, const int3
     return int(__builtin_ctzll(m));
   };
   // the padded row of each slot's intermediate, from a scan of sorted_ids by
-  // this wave (into this wave's part of slot_row: no barrier needed)
-  const int npad = *g.num_padded;
+  // this wave (into this wave's part of slot_row: no barrier needed), or,
+  // with one block per assignment, row 16 f
   int* rows = slot_row + wave * KMAX;
-  for (int r0 = 0; r0 < npad; r0 += 64) {
-    const int r = r0 + lane;
-    const int f = r < npad ? g.sorted_ids[r] : g.A;
-    if (f >= f0 && f < f0 + Kp) rows[f - f0] = r;
+  if (g.slot_ids) {
+    if (lane < Kp) rows[lane] = (f0 + lane) * 16;
+  } else {
+    const int npad = *g.num_padded;
+    for (int r0 = 0; r0 < npad; r0 += 64) {
+      const int r = r0 + lane;
+      const int f = r < npad ? g.sorted_ids[r] : g.A;
+      if (f >= f0 && f < f0 + Kp) rows[f - f0] = r;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes done (lgkmcnt 0)
   __builtin_amdgcn_wave_barrier();
@@ -565,9 +576,11 @@ dim3 stream_grid(const GemmCfg& c, int tiles, int64_t blocks) {
 hipError_t launch_gemm1(const moe_problem& p, const Plan& q, const void* x, const void* xs,
                         const moe_weights& w, const int32_t* sorted_ids,
                         const int32_t* block_expert, const int32_t* num_padded, void* a2,
-                        void* a2s, hipStream_t stream) {
+                        void* a2s, hipStream_t stream, const int32_t* slot_ids) {
   if (q.max_blocks == 0) return hipSuccess;
   GemmArgs a{};
+  a.E = p.E;
+  a.slot_ids = slot_ids;
   a.b = static_cast<const uint8_t*>(x);
   a.b_scale = static_cast<const float*>(xs);
   a.b_sc8 = static_cast<const uint8_t*>(xs);
@@ -642,9 +655,11 @@ hipError_t launch_gemm2_combine_tok(const moe_problem& p, const Plan& q, const v
                                    const void* a2s, const moe_weights& w,
                                    const int32_t* sorted_ids, const int32_t* num_padded,
                                    const int32_t* topk_ids, const float* topk_w, uint16_t* out,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, bool slot_rows) {
   if (p.T == 0) return hipSuccess;
   GemmArgs a{};
+  a.E = p.E;
+  a.slot_ids = slot_rows ? topk_ids : nullptr;
   a.b = static_cast<const uint8_t*>(a2);
   a.b_scale = static_cast<const float*>(a2s);
   a.b_sc8 = static_cast<const uint8_t*>(a2s);

@@ -25,6 +25,11 @@ struct GemmArgs {
   int K, N, I, H, Kp, A, steps, tiles;
   int slices;                // tiled kernel: workgroups along the weight rows
   int nwg;                   // tiled kernel: real workgroups (grid is padded to 8)
+  int E;                     // expert slots
+  // one-token decode (Plan::slot_rows): the expert of each assignment; GEMM1
+  // block b holds assignment b alone and the intermediate of slot f sits at
+  // row 16 f (null: blocks and rows from the alignment)
+  const int32_t* slot_ids;
 };
 
 // Per-format constants: u32x4 loads per A / B fragment, bytes per A

@@ -53,6 +53,8 @@ struct Plan {
   int32_t a2_elem = 0;     // bytes per intermediate element
   GemmCfg g1{}, g2{};
   bool g2_tok = false;     // GEMM2 and the combine token by token, in one launch
+  bool slot_rows = false;  // moe_forward on one token: GEMM1 block b holds assignment b
+                           // alone, no alignment (the rows of slot f start at 16 f)
   int32_t chunk_T = 0;     // tokens per moe_forward pass (the workspace below is one pass's)
   // moe_forward workspace layout (byte offsets, 256-B aligned), for a pass of
   // chunk_T tokens
