@@ -189,8 +189,9 @@ int make_plan(const moe_problem* p, Plan* plan) {
     // launch (every weight tile a token routes to is streamed for it alone,
     // which at this size is what the expert-major kernel does too)
     q.g2_tok = q.A <= kTokMaxAssign && p->T <= kTokMaxTokens;
-    // one token: every expert has at most one of its rows, so a block per
-    // assignment is what the alignment would produce (in another order)
+    // one token: a block per assignment, each row with the arithmetic it
+    // has in the aligned blocks (the routed experts of a token are distinct;
+    // an expert repeated in caller-given ids streams its weights per slot)
     q.slot_rows = q.g2_tok && p->T == 1 && p->block_m == 0;
   } else {
     // fp8 / int4 / MX weights at 128-row blocks: weights and tokens staged in

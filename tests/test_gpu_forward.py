@@ -339,3 +339,28 @@ def test_token_major_gemm2_equals_expert_major_path(quant, act):
     assert torch.equal(one.view(torch.int16), three[:1].view(torch.int16))
     parity(cfg, W, layer, tok["x_bits"][:2], tok["logits"][:2], sc["a1"], sc["a2"],
            label=f"token-major {quant} {act}")
+
+
+@pytest.mark.parametrize("quant,routed", [("bf16", True), ("bf16", False), ("fp8_tensor", True),
+                                          ("fp8_tensor", False), ("w4a8", False),
+                                          ("mxfp4", True)])
+def test_one_token_forward_equals_components(quant, routed):
+    """One token through moe_forward (a GEMM1 block per assignment, no
+    alignment; with caller-given ids an expert repeated and a slot masked)
+    against the separate entry points (aligned blocks), bit for bit, and the
+    oracle."""
+    cfg = ad_hoc(97, quant, "silu", H=256, I=256, E_routed=12, top_k=4, n_shared=1)
+    W = synth.make_weights(cfg, seed=131)
+    tok = synth.make_tokens(cfg, 1, seed=132)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
+    say(f"one token {quant} routed={routed}")
+    if routed:
+        parity(cfg, W, layer, tok["x_bits"], tok["logits"], sc["a1"], sc["a2"],
+               label=f"one token {quant}")
+    else:
+        ids = np.array([[7, 7, -1, 3, 12]], dtype=np.int32)   # repeat, mask, shared slot
+        w = np.array([[0.5, 0.25, 0.9, 0.125, 1.0]], dtype=np.float32)
+        parity(cfg, W, layer, tok["x_bits"], None, sc["a1"], sc["a2"], topk_ids=ids, topk_w=w,
+               label=f"one token prerouted {quant}")
+
