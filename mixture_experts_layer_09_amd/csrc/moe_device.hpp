@@ -102,32 +102,33 @@ __device__ __forceinline__ uint32_t mx8x4(float a, float b, float c, float d, in
                 __builtin_amdgcn_ldexpf(c, -X), __builtin_amdgcn_ldexpf(d, -X));
 }
 
-// Signed int4 -> e4m3 codes, exact.  `nib` holds one nibble value (0..15,
-// two's complement) in the low 4 bits of each byte; the result holds the
-// e4m3 code of each.  Two byte-permute table lookups (values 0..7 and
-// -8..-1) and a per-byte select on the nibble's sign bit.
-__device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t nib) {
-  const uint32_t sel = nib & 0x07070707u;
+// Signed int4 -> e4m3 codes, exact.  Bits 0-3 of each byte of `v` hold one
+// nibble value (two's complement; bits 4-7 are ignored); the result holds
+// the e4m3 code of each.  Two byte-permute table lookups on bits 0-2 (values
+// 0..7 and -8..-1), and a per-byte select on the sign (bit 3) through a
+// third permute: selector byte 5 reads a zero byte of the zero sources,
+// selector 13 yields 0xFF.
+__device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t v) {
+  const uint32_t sel = v & 0x07070707u;
   // codes of 0,1,2,3 | 4,5,6,7
   const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
   // codes of -8,-7,-6,-5 | -4,-3,-2,-1
   const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, sel);
-  // 0xFF in the bytes whose bit 3 (the sign) is set: per byte 2^8 - 2^0,
-  // written as (t << 5) - (t >> 3) so no carry crosses a byte
-  const uint32_t t = nib & 0x08080808u;
-  const uint32_t m = (t << 5) - (t >> 3);
+  // 0xFF in the bytes whose sign bit is set
+  const uint32_t m = __builtin_amdgcn_perm(0u, 0u, (v & 0x08080808u) | 0x05050505u);
   return (neg & m) | (pos & ~m);
 }
 
 // 16 bytes of packed int4 (32 values) -> 32 e4m3 codes.  Byte b of input
 // dword q holds value 8q + b in its low nibble and 8q + 4 + b in its high
-// nibble, so output dword 2q takes the low nibbles and 2q + 1 the high ones.
+// nibble, so output dword 2q takes the low nibbles and 2q + 1 the high ones
+// (shifted down by 4: each byte's bits 0-3 are then its high nibble).
 __device__ __forceinline__ i32x8 int4x32_to_e4m3(const u32x4& v) {
   i32x8 r;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    r[2 * q] = int32_t(int4x4_to_e4m3(v[q] & 0x0F0F0F0Fu));
-    r[2 * q + 1] = int32_t(int4x4_to_e4m3((v[q] >> 4) & 0x0F0F0F0Fu));
+    r[2 * q] = int32_t(int4x4_to_e4m3(v[q]));
+    r[2 * q + 1] = int32_t(int4x4_to_e4m3(v[q] >> 4));
   }
   return r;
 }
