@@ -264,8 +264,11 @@ def parity(cfg, W, layer, x_bits, logits=None, a1=None, a2=None, topk_ids=None, 
     layer.gemm1(T, x, b)
     layer.gemm2(T, b)
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), b["out"].view(torch.int16)), \
-        f"{label}: moe_forward differs from the separate entry points"
+    same = out.view(torch.int16) == b["out"].view(torch.int16)
+    assert bool(same.all()), \
+        (f"{label}: moe_forward differs from the separate entry points at "
+         f"{int((~same).sum())} of {same.numel()} outputs, first at "
+         f"{[tuple(i) for i in (~same).nonzero()[:4].tolist()]}")
     ref = oracle_forward(cfg, W, x_bits, logits, a1, a2, topk_ids=topk_ids,
                          topk_w=None if topk_w is None else np.asarray(topk_w, np.float64),
                          return_intermediate=bool(check_a2))

@@ -364,3 +364,31 @@ def test_one_token_forward_equals_components(quant, routed):
         parity(cfg, W, layer, tok["x_bits"], None, sc["a1"], sc["a2"], topk_ids=ids, topk_w=w,
                label=f"one token prerouted {quant}")
 
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_one_token_back_to_back(cid):
+    """One-token passes (a GEMM1 block per assignment, no alignment) on three
+    different tokens, enqueued 8 times over without synchronisation: every
+    output equals the separate entry points' for its token, bit for bit (no
+    pass reads a workspace value left by an earlier one)."""
+    cfg = synth.CONFIGS[cid]
+    W = weights_for(cfg)
+    toks = [synth.make_tokens(cfg, 1, seed=700 + k) for k in range(3)]
+    sc = synth.make_act_scales(cfg, toks[0]["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
+    say(f"one token back to back {cfg.name}")
+    xs = [dev(t["x_bits"]) for t in toks]
+    lgs = [dev(t["logits"]) for t in toks]
+    refs = []
+    for x, lg in zip(xs, lgs):
+        b = layer.buffers(1)
+        layer.prepare(1, lg, x, b)
+        layer.gemm1(1, x, b)
+        layer.gemm2(1, b)
+        refs.append(b["out"].clone())
+    outs = [(k, layer.forward(xs[k], lgs[k])) for _ in range(8) for k in range(3)]
+    torch.cuda.synchronize()
+    assert len({r.view(torch.int16).cpu().numpy().tobytes() for r in refs}) == 3
+    for n, (k, o) in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), refs[k].view(torch.int16)), f"pass {n} token {k}"
+

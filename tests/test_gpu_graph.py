@@ -11,7 +11,8 @@ from gpu_cases import build_layer, dev, say, weights_for
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cid,quant,M", [(2, None, 64), (2, "mxfp4", 8), (3, None, 16)])
+@pytest.mark.parametrize("cid,quant,M", [(2, None, 64), (2, "mxfp4", 8), (3, None, 16),
+                                        (2, None, 1), (4, None, 1)])
 def test_captured_forward_replays_exactly(cid, quant, M):
     import dataclasses
     cfg = synth.CONFIGS[cid]
@@ -21,7 +22,8 @@ def test_captured_forward_replays_exactly(cid, quant, M):
     W = weights_for(cfg)
     tok = synth.make_tokens(cfg, M)
     other = synth.make_tokens(cfg, M, seed=4321)
-    layer = build_layer(cfg, W)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
     x, lg = dev(tok["x_bits"]), dev(tok["logits"])
     x2, lg2 = dev(other["x_bits"]), dev(other["logits"])
     out = torch.empty((M, cfg.H), dtype=torch.bfloat16, device="cuda")
