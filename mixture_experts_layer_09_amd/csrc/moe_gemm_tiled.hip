@@ -236,7 +236,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
 template <int Q, int WC, int NWV, int WT = 4, int NW = 8> struct LdsCfg {
   static constexpr int WR = NWV / WC;
   static constexpr int TILES = WT * WR, NT = NW * WC;  // weight / token tiles per workgroup
-  static constexpr int A_BYTES = TILES * QT<Q>::FRAG;
+  // A stage holds 128 bytes of K per row: one fp8 / int4 / MX k-step, two
+  // bf16 k-steps (two 1 KiB fragments of each weight tile, contiguous in the
+  // packed weights).  SF: a weight tile's bytes per stage, SAV: its 16-byte
+  // lane loads.
+  static constexpr int SF = Q == MOE_QUANT_BF16 ? 2048 : QT<Q>::FRAG;
+  static constexpr int SAV = SF / 1024;
+  static constexpr int A_BYTES = TILES * SF;
   static constexpr int B_BYTES = NT * 2048;
   // scales of a stage: fp8 block / int4 group scales in 1 KiB; MX: E8M0
   // weight scales (64 bytes per tile; every wave loads 256 bytes per load
@@ -253,7 +259,7 @@ template <int Q, int WC, int NWV, int WT = 4, int NW = 8> struct LdsCfg {
   static constexpr int SMAX = 4;
   static constexpr int S = (160 * 1024 - 4096) / STAGE < SMAX ? (160 * 1024 - 4096) / STAGE : SMAX;
   // loads per wave per stage: weight fragments, token fragments, scales
-  static constexpr int LOADS = TILES * QT<Q>::AV / NWV + NT * 2 / NWV + SC_LOADS;
+  static constexpr int LOADS = TILES * SAV / NWV + NT * 2 / NWV + SC_LOADS;
   static_assert(S * STAGE <= 160 * 1024 - 4096, "stage buffers exceed the LDS");
   static_assert(Q != MOE_QUANT_FP8_BLOCK || WC == 1,
                 "block scales: one workgroup spans the 128 output channels of a group");
@@ -363,7 +369,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
     const int tile0 = wg_tile0 + wr * WT;
     const bool active = tile0 < g.tiles && ct > 0;
     const int kblocks = g.K / 128;
-    const int nst = g.K / 128;
+    const int nst = g.K * T::EB / 128;  // stages of 128 bytes of K per row
     constexpr bool MX = kMx<Q>;
     constexpr int BRUN = MX ? 16 : 32, BHALF = MX ? kMxHalfStride : 16;
 
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       } else {
         brow = row0 + r;
       }
-      bsrc[q] = uint32_t(brow) * uint32_t(g.K) + grp * BRUN;
+      bsrc[q] = uint32_t(brow) * uint32_t(g.K * T::EB) + grp * BRUN;
     }
     // scales of a stage: fp8-block token-row scales (waves 1, 2) and weight
     // scales (every other wave, the same values); W4A8 group scales (every
@@ -449,9 +455,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
   #pragma unroll
       for (int r = 0; r < LA; ++r)
   #pragma unroll
-        for (int v = 0; v < T::AV; ++v)
-          ld_lds16(asrc[r] + size_t(st) * T::FRAG + v * 1024,
-                     base + (wave * LA + r) * T::FRAG + v * 1024);
+        for (int v = 0; v < C::SAV; ++v)
+          ld_lds16(asrc[r] + size_t(st) * C::SF + v * 1024,
+                     base + (wave * LA + r) * C::SF + v * 1024);
   #pragma unroll
       for (int q = 0; q < LB; ++q)
   #pragma unroll
@@ -479,24 +485,50 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
     // indexes the stage array once with a whole offset: a longer chain of
     // pointer steps hides from the compiler which array a read touches, and
     // it then waits for every direct-to-LDS load in flight before the read.
-    const int a_off = wr * WT * T::FRAG + lane * 16;
+    const int a_off = wr * WT * C::SF + lane * 16;
     const int b_off = C::A_BYTES + wc * NW * 2048 + lane * 16;
+    // bf16: a token tile's stage holds, at h * 1024 + 16 L, bytes 32 (L / 16)
+    // + 16 h of row L % 16 (the fp8 fragment order); the 16 x 16 x 32 MFMA's
+    // lane (g, r) needs, for the stage's k-step j, bytes 64 j + 16 g of row r:
+    // L = 16 (2 j + g / 2) + r, h = g % 2
+    const int bf_off = C::A_BYTES + wc * NW * 2048 + (grp & 1) * 1024 + (grp >> 1) * 256 + lrow * 16;
     auto rd16 = [](const uint8_t* base, int off) {
       return *reinterpret_cast<const u32x4*>(base + off);
     };
     auto compute = [&](auto bufc) {
       const uint8_t* base = stage_buf(bufc);
+      if constexpr (Q == MOE_QUANT_BF16) {
+        // two k-steps of 32 per stage, in k order
+        u32x4 a2[WT][2];
+  #pragma unroll
+        for (int r = 0; r < WT; ++r)
+  #pragma unroll
+          for (int j = 0; j < 2; ++j) a2[r][j] = rd16(base, a_off + r * C::SF + j * 1024);
+  #pragma unroll
+        for (int c = 0; c < NW; ++c) {
+          if (c < ct) {
+  #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const u32x4 bb = rd16(base, bf_off + c * 2048 + j * 512);
+  #pragma unroll
+              for (int r = 0; r < WT; ++r) acc[r][c] = mfma_bf16(a2[r][j], bb, acc[r][c]);
+            }
+          }
+          if constexpr (NW > 8) __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
       const float* sc = reinterpret_cast<const float*>(base + C::A_BYTES + C::B_BYTES);
       i32x8 a8[WT];
   #pragma unroll
       for (int r = 0; r < WT; ++r) {
         if constexpr (MX) {
-          a8[r] = mx_weight_operand<Q>(rd16(base, a_off + r * T::FRAG),
-                                       rd16(base, a_off + r * T::FRAG + (T::AV - 1) * 1024));
+          a8[r] = mx_weight_operand<Q>(rd16(base, a_off + r * C::SF),
+                                       rd16(base, a_off + r * C::SF + (T::AV - 1) * 1024));
         } else if (Q == MOE_QUANT_W4A8) {
-          a8[r] = int4x32_to_e4m3(rd16(base, a_off + r * T::FRAG));
+          a8[r] = int4x32_to_e4m3(rd16(base, a_off + r * C::SF));
         } else {
-          a8[r] = fp8_pair(rd16(base, a_off + r * T::FRAG), rd16(base, a_off + r * T::FRAG + 1024));
+          a8[r] = fp8_pair(rd16(base, a_off + r * C::SF), rd16(base, a_off + r * C::SF + 1024));
         }
       }
       float ws[WT];
@@ -644,7 +676,7 @@ int persistent_slots() {
 template <int PHASE, int Q, int ACT>
 hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
   const dim3 grid(unsigned((a.nwg + 7) / 8 * 8)), block(256);
-  if constexpr (Q != MOE_QUANT_BF16) {
+  {
     if (c.kind == 2 || c.kind == 3) {
       // kind 3: one workgroup per CU (the stage buffers take most of the LDS)
       const dim3 pgrid(c.kind == 3 ? std::min<unsigned>(grid.x, unsigned(persistent_slots()))
@@ -671,7 +703,7 @@ hipError_t dispatch_tiled(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
           return hipGetLastError();
         }
       }
-      if constexpr (Q == MOE_QUANT_FP8_TENSOR || kMx<Q>) {
+      if constexpr (Q == MOE_QUANT_FP8_TENSOR || kMx<Q> || Q == MOE_QUANT_BF16) {
         // 8 waves, 256 x 256: one workgroup per tile (the persistent loop's
         // state does not fit the registers of 8 waves of 4 x 8 tiles)
         if (c.nt == 16 && c.kind == 2) {

@@ -145,13 +145,16 @@ int make_plan(const moe_problem* p, Plan* plan) {
   // ---- tile table: the alignment block follows the expected rows per
   // expert.  Decode-sized problems stream weights 16 token rows at a time;
   // with many rows per expert the tiled kernels stage 128 token rows in LDS
-  // and reuse every weight fragment across them; fp8 per-tensor, int4 and MX
-  // weights with 256 or more rows per expert take 256 token rows per block,
-  // so that each weight byte brought into the LDS (and each int4 fragment
-  // converted to e4m3) serves twice the tokens.
+  // and reuse every weight fragment across them; bf16, fp8 per-tensor, int4
+  // and MX weights with 256 or more rows per expert take 256 token rows per
+  // block, so that each weight byte brought into the LDS (and each int4
+  // fragment converted to e4m3) serves twice the tokens.
   const int64_t rows_per_expert = q.A / std::max(1, p->E);
-  const bool wide_ok =
-      p->quant == MOE_QUANT_FP8_TENSOR || p->quant == MOE_QUANT_W4A8 || quant_is_mx(p->quant);
+  // the LDS pipeline stages 128 bytes of K per row: bf16 needs I % 64 == 0
+  // for GEMM2 (the other formats pad I to 128)
+  const bool lds_ok = p->quant != MOE_QUANT_BF16 || p->I % 64 == 0;
+  const bool wide_ok = (p->quant == MOE_QUANT_BF16 && lds_ok) || p->quant == MOE_QUANT_FP8_TENSOR ||
+                       p->quant == MOE_QUANT_W4A8 || quant_is_mx(p->quant);
   if (p->block_m != 0) {
     q.BM = p->block_m;
   } else if (rows_per_expert >= kWideMinRows && wide_ok) {
@@ -163,7 +166,8 @@ int make_plan(const moe_problem* p, Plan* plan) {
   }
   if (q.BM == 256 && !wide_ok)
     return fail(MOE_ERR_UNSUPPORTED,
-                "block_m = 256 runs for the fp8 per-tensor, int4 (W4A8) and MX modes only");
+                "block_m = 256 runs for the bf16 (I a multiple of 64), fp8 per-tensor, int4 (W4A8) "
+                "and MX modes only");
   if (quant_is_mx(p->quant) && q.BM == 64)
     return fail(MOE_ERR_UNSUPPORTED, "the MX modes run block_m = 16, 128 and 256");
   const int64_t nz = std::min<int64_t>(p->E, q.A);
@@ -194,12 +198,12 @@ int make_plan(const moe_problem* p, Plan* plan) {
     // an expert repeated in caller-given ids streams its weights per slot)
     q.slot_rows = q.g2_tok && p->T == 1 && p->block_m == 0;
   } else {
-    // fp8 / int4 / MX weights at 128-row blocks: weights and tokens staged in
-    // LDS by direct-to-LDS loads, several k-steps in flight, one persistent
-    // workgroup per CU taking the tiles in rounds (kind 3).  256-row blocks:
-    // 8 waves; int4 persistent, fp8 per-tensor and MX one workgroup per tile
-    // (kind 2).  bf16 weights: the register-staged tile (kind 1).
-    const bool lds = q.BM >= 128 && p->quant != MOE_QUANT_BF16;
+    // 128-row blocks: weights and tokens staged in LDS by direct-to-LDS loads,
+    // several stages in flight, one persistent workgroup per CU taking the
+    // tiles in rounds (kind 3).  256-row blocks: 8 waves; int4 persistent,
+    // bf16, fp8 per-tensor and MX one workgroup per tile (kind 2).  64-row
+    // blocks: the register-staged tile (kind 1).
+    const bool lds = q.BM >= 128 && lds_ok;
     const int wide_kind = p->quant == MOE_QUANT_W4A8 ? 3 : 2;
     q.g1 = GemmCfg{lds ? (q.BM == 256 ? wide_kind : 3) : 1, q.BM / 16, 4, 1, 4};
     q.g2 = q.g1;

@@ -82,10 +82,12 @@ def test_valid_problems(plan):
     (dict(quant=6), moe.MOE_ERR_INVALID_ARG),
     (dict(quant="mxfp8", block_m=64), moe.MOE_ERR_UNSUPPORTED),   # MX: 16 or 128
     (dict(quant="mxfp4", block_m=64), moe.MOE_ERR_UNSUPPORTED),
-    (dict(quant="bf16", block_m=256), moe.MOE_ERR_UNSUPPORTED),
+    (dict(quant="fp8_block", block_m=256), moe.MOE_ERR_UNSUPPORTED),
+    (dict(I=96, block_m=256), moe.MOE_ERR_UNSUPPORTED),            # bf16 LDS tiles: I % 64
     (dict(quant="mxfp4", I=160), moe.MOE_ERR_ALIGNMENT),          # MX needs 128
     (dict(block_m=17), moe.MOE_ERR_INVALID_ARG),
-    (dict(block_m=256), moe.MOE_ERR_UNSUPPORTED),                 # 256: fp8 per-tensor, W4A8
+    (dict(quant="fp8_block", act="relu2", block_m=256),
+     moe.MOE_ERR_UNSUPPORTED),                                     # 256: not block scales
     (dict(H=200), moe.MOE_ERR_ALIGNMENT),
     (dict(I=500), moe.MOE_ERR_ALIGNMENT),                       # gated bf16 needs 32
     (dict(I=500, act="gelu_tanh"), moe.MOE_ERR_ALIGNMENT),

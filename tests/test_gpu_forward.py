@@ -68,6 +68,23 @@ def test_forward_gelu_tanh_full_size(cid, M):
     _full(cfg, M, f"gelu_tanh {cfg.name} M={M}")
 
 
+# bf16 weights at prefill sizes on the decode configuration's shapes (hidden
+# 2048, 128 experts, top-8, intermediate 768): 64 rows per expert (128-row
+# blocks, the 4-wave LDS pipeline, persistent) and 256 (256-row blocks, the
+# 8-wave 256 x 256 tile).
+BF16_PREFILL = [(2, 1024), (2, 4096)]
+
+
+@pytest.mark.parametrize("cid,M", BF16_PREFILL, ids=[f"cfg{c}-M{m}" for c, m in BF16_PREFILL])
+def test_forward_bf16_prefill_full_size(cid, M):
+    cfg = synth.CONFIGS[cid]
+    p = moe.problem(T=M, H=cfg.H, I=cfg.I, E_routed=cfg.E_routed, top_k=cfg.top_k, act=cfg.act,
+                    quant=cfg.quant, n_shared=cfg.n_shared)
+    assert moe.block_m(p) == (256 if M >= 4096 else 128)
+    say(f"forward bf16 prefill {cfg.name} M={M}")
+    _full(cfg, M, f"bf16 prefill {cfg.name} M={M}")
+
+
 # The MX modes at full size: the decode shape (hidden 2048, 128 experts,
 # top-8, intermediate 768), the fp8 block-scale prefill shape (hidden 2048,
 # 512 + 1 experts, top-10, intermediate 512) and the W4A8 shape, with MXFP8
@@ -203,7 +220,7 @@ def test_invalid_call_enqueues_nothing():
 
 TILED = [(q, a, bm) for q in ("bf16", "fp8_tensor", "fp8_block", "w4a8")
          for a in ("silu", "relu2", "gelu_tanh") for bm in (64, 128)] + \
-        [(q, a, 256) for q in ("fp8_tensor", "w4a8") for a in ("silu", "relu2", "gelu_tanh")] + \
+        [(q, a, 256) for q in ("bf16", "fp8_tensor", "w4a8") for a in ("silu", "relu2", "gelu_tanh")] + \
         [(q, a, bm) for q in ("mxfp8", "mxfp4") for a in ("silu", "relu2", "gelu_tanh")
          for bm in (128, 256)]
 
@@ -225,10 +242,10 @@ def test_forward_tiled_ragged(quant, act, bm):
            label=f"tiled {quant} {act} bm={bm}")
 
 
-@pytest.mark.parametrize("quant,act", [(q, a) for q in ("fp8_tensor", "w4a8", "mxfp8", "mxfp4")
+@pytest.mark.parametrize("quant,act", [(q, a) for q in ("bf16", "fp8_tensor", "w4a8", "mxfp8", "mxfp4")
                                        for a in ("silu", "relu2", "gelu_tanh")])
 def test_forward_wide_blocks_by_default(quant, act):
-    """fp8 per-tensor, int4 and MX with 256+ rows per expert take 256-row blocks
+    """bf16, fp8 per-tensor, int4 and MX with 256+ rows per expert take 256-row blocks
     by themselves: several full blocks per expert, ragged last blocks, and
     blocks whose second half of token tiles is empty or partly filled."""
     cfg = ad_hoc(94, quant, act, H=512, I=384, E_routed=4, top_k=2, n_shared=1)
