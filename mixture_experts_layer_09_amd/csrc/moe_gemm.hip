@@ -291,21 +291,23 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < WT; ++j) {
       const int n = (tile0 + j) * 16 + grp * 4;
-      *reinterpret_cast<f32x4*>(g.out + (size_t(f) * g.H + n) * 4) = acc[j] * wgt;
+      store_row4<Q>(g.out, size_t(f), g.H, n, acc[j] * wgt);
     }
   }
 }
 
-// out[t][:] = bf16(sum over valid slots j of y[t*K' + j][:]) with y in fp32,
-// one thread per 8 hidden values.  The rows of up to 8 slots are loaded
+// out[t][:] = bf16(sum over valid slots j of y[t*K' + j][:]) with y in fp32
+// (BF: bf16, the rows of int4 weights), summed in fp32, one thread per 8
+// hidden values.  The rows of up to 8 slots are loaded
 // before any is added, so each thread has 16 loads in flight; the sum still
 // runs in slot order.  Every slot's row lies inside y, so the rows are
 // loaded together with the ids rather than after them; a slot whose id is
 // outside [0, E) (never written by GEMM2) is loaded and left out of the sum.
 // (4 or 16 values per thread, or plain instead of non-temporal loads, were
 // measured slower.)
+template <bool BF>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
-                                                     const float* __restrict__ y,
+                                                     const void* __restrict__ yv,
                                                      uint16_t* __restrict__ out, int T, int H,
                                                      int Kp, int E) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -322,9 +324,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       const int e = j < Kp ? ids[size_t(t) * Kp + j] : -1;
       ok[u] = e >= 0 && e < E;
       if (j < Kp) {
-        const float* row = y + (size_t(t) * Kp + j) * H + c;
-        v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row));
-        v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4));
+        const size_t at = (size_t(t) * Kp + j) * H + c;
+        if constexpr (BF) {
+          const u32x4 b = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(yv) + at));
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            v[u][0][2 * k] = bf16_to_f32(b[k] & 0xFFFFu);
+            v[u][0][2 * k + 1] = bf16_to_f32(b[k] >> 16);
+            v[u][1][2 * k] = bf16_to_f32(b[2 + k] & 0xFFFFu);
+            v[u][1][2 * k + 1] = bf16_to_f32(b[2 + k] >> 16);
+          }
+        } else {
+          const float* row = static_cast<const float*>(yv) + at;
+          v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row));
+          v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4));
+        }
       }
     }
 #pragma unroll
@@ -510,10 +525,15 @@ __global__ __launch_bounds__(1024) void gemm2_combine_tok(GemmArgs g, const int3
         f32x4 a = red[0][j][grp];
 #pragma unroll
         for (int k = 1; k < KS; ++k) a += red[k][j][grp];
-        // the row value first (as GEMM2 stores it), then the slot-order sum:
-        // kept apart so that no fused multiply-add changes the rounding
+        // the row value first (as GEMM2 stores it, bf16 for int4 weights),
+        // then the slot-order sum: kept apart so that no fused multiply-add
+        // changes the rounding
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sum[i] = __fadd_rn(sum[i], __fmul_rn(a[i], wgt));
+        for (int i = 0; i < 4; ++i) {
+          float r = __fmul_rn(a[i], wgt);
+          if (kRowsBf16<Q>) r = bf16_to_f32(bf16_bits(r));
+          sum[i] = __fadd_rn(sum[i], r);
+        }
       }
     }
     if (col0) {
@@ -708,8 +728,12 @@ hipError_t launch_combine(const moe_problem& p, const Plan& q, const int32_t* to
                           const float* y, uint16_t* out, hipStream_t stream) {
   const int64_t n = int64_t(p.T) * (p.H / 8);
   if (n == 0) return hipSuccess;
-  combine_kernel<<<unsigned((n + 255) / 256), 256, 0, stream>>>(topk_ids, y, out, p.T, p.H, q.Kp,
-                                                                p.E);
+  if (rows_bf16(p.quant))
+    combine_kernel<true><<<unsigned((n + 255) / 256), 256, 0, stream>>>(topk_ids, y, out, p.T,
+                                                                      p.H, q.Kp, p.E);
+  else
+    combine_kernel<false><<<unsigned((n + 255) / 256), 256, 0, stream>>>(topk_ids, y, out, p.T,
+                                                                       p.H, q.Kp, p.E);
   return hipGetLastError();
 }
 

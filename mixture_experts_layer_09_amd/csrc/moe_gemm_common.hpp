@@ -85,6 +85,25 @@ __device__ __forceinline__ i32x8 fp8_pair(const u32x4& lo, const u32x4& hi) {
   return r;
 }
 
+// GEMM2's per-assignment rows, summed by the combine: fp32, or bf16 for int4
+// weights (W4A8), whose outputs the method holds to a relative L2 error of
+// 3e-2 only -- rounding the ~8 weighted rows of a token to bf16 adds ~1e-3 --
+// so that the rows' round trip through HBM moves half the bytes.
+template <int Q> constexpr bool kRowsBf16 = rows_bf16(Q);
+
+// Four consecutive values of row f (element n) of the per-assignment rows y.
+template <int Q>
+__device__ __forceinline__ void store_row4(uint8_t* y, size_t f, int H, int n, const f32x4& v) {
+  if constexpr (kRowsBf16<Q>) {
+    u32x2 o;
+    o[0] = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+    o[1] = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+    *reinterpret_cast<u32x2*>(y + (f * H + n) * 2) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(y + (f * H + n) * 4) = v;
+  }
+}
+
 // Gated activations pair a gate and an up channel; relu2 is the one that is not.
 constexpr bool act_gated(int act) { return act != MOE_ACT_RELU2; }
 

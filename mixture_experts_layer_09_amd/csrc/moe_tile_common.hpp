@@ -162,7 +162,7 @@ __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[W
 #pragma unroll
         for (int r = 0; r < WT; ++r) {
           const int n = (tile0 + r) * 16 + grp * 4;
-          *reinterpret_cast<f32x4*>(g.out + (size_t(f) * g.H + n) * 4) = acc[r][c] * wgt;
+          store_row4<Q>(g.out, size_t(f), g.H, n, acc[r][c] * wgt);
         }
       }
     }
