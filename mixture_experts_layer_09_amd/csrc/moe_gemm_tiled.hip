@@ -213,11 +213,15 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-pipelined variant for the fp8 and W4A8 modes.  Weight fragments and
-// token rows go from global memory straight into LDS (global_load_lds with
-// 16 bytes per lane: lane l's bytes land at base + 16 l, which is exactly the
-// lane order of a pre-tiled weight fragment and of an MFMA B fragment), so
-// S stages can be in flight without holding registers.  Per stage a
+// LDS-pipelined variant for blocks of 128 or more token rows (fp8, W4A8, MX,
+// and bf16 where the intermediate size is a multiple of 64).  Weight
+// fragments and token rows go from global memory straight into LDS
+// (global_load_lds with 16 bytes per lane: lane l's bytes land at
+// base + 16 l, which is exactly the lane order of a pre-tiled weight fragment
+// and of an MFMA B fragment), so S stages can be in flight without holding
+// registers.  A stage covers 128 bytes of K per row: one 128-k step of the
+// fp8/fp4 MFMA, or, in bf16, 64 k as two 32-k MFMA steps whose A and B
+// halves each lane reads at its own LDS offset.  Per stage a
 // workgroup (4 waves, 16 weight row tiles x 8 token tiles) loads 16 weight
 // fragments, 8 token fragments and the stage's scales; every wave issues the
 // same number of loads, waits for its loads of the oldest stage, then a
