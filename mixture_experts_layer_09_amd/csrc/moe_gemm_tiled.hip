@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
       const int f = g.sorted_ids[row0 + r];
       brow = f < g.A ? f / g.Kp : 0;
     } else {
-      brow = row0 + r;
+      brow = r < nvalid ? row0 + r : row0;
     }
     bofs[j] = uint32_t(brow) * uint32_t(g.K * T::EB) + c16 * 16;
     lofs[j] = r * LROW + c16 * 16;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled(GemmArgs g) {
   // FP8_BLOCK: the B row scale of row `tid` per stage
   int bs_row = 0;
   if (Q == MOE_QUANT_FP8_BLOCK && tid < BM)
-    bs_row = PHASE == 1 ? (f_mine < g.A ? f_mine / g.Kp : 0) : row0 + tid;
+    bs_row = PHASE == 1 ? (f_mine < g.A ? f_mine / g.Kp : 0) : (tid < nvalid ? row0 + tid : row0);
   const int kblocks = g.K / 128;
 
   const size_t ebytes = size_t(g.tiles) * g.steps * T::FRAG;
@@ -390,6 +390,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
       const int t = min(wg_tile0 + wave * LA + r, g.tiles - 1);
       asrc[r] = wexp + size_t(t) * g.steps * T::FRAG + lane * 16;
     }
+    // Padding rows (past the block's real rows) read a real row instead of
+    // their own: GEMM1 reads token row 0, GEMM2 the block's first row, so
+    // their loads hit lines the L1 already holds and bring nothing into L2.
+    // Their products are never stored.
     uint32_t bsrc[LB];
   #pragma unroll
     for (int q = 0; q < LB; ++q) {
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
         const int f = g.sorted_ids[row0 + r];
         brow = f < g.A ? f / g.Kp : 0;
       } else {
-        brow = row0 + r;
+        brow = r < nvalid ? row0 + r : row0;
       }
       bsrc[q] = uint32_t(brow) * uint32_t(g.K * T::EB) + grp * BRUN;
     }
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
           const int f = g.sorted_ids[row0 + r];
           brow = f < g.A ? f / g.Kp : 0;
         } else {
-          brow = row0 + r;
+          brow = r < nvalid ? row0 + r : row0;
         }
         ssrc = g.b_scale + size_t(brow) * kblocks;
         sdst = 256 + (wave - 1) * 256;
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_lds(GemmArgs g) {
         const int f = r < BM ? g.sorted_ids[row0 + r] : g.A;
         brow = f < g.A ? f / g.Kp : 0;
       } else {
-        brow = r < BM ? row0 + r : row0;
+        brow = r < nvalid ? row0 + r : row0;
       }
       mx_tsrc = g.b_sc8 + size_t(brow) * (g.K / 32);
     }
