@@ -200,12 +200,10 @@ int make_plan(const moe_problem* p, Plan* plan) {
   } else {
     // 128-row blocks: weights and tokens staged in LDS by direct-to-LDS loads,
     // several stages in flight, one persistent workgroup per CU taking the
-    // tiles in rounds (kind 3).  256-row blocks: 8 waves; int4 persistent,
-    // bf16, fp8 per-tensor and MX one workgroup per tile (kind 2).  64-row
-    // blocks: the register-staged tile (kind 1).
+    // tiles in rounds (kind 3).  256-row blocks: 8 waves, one workgroup per
+    // tile (kind 2).  64-row blocks: the register-staged tile (kind 1).
     const bool lds = q.BM >= 128 && lds_ok;
-    const int wide_kind = p->quant == MOE_QUANT_W4A8 ? 3 : 2;
-    q.g1 = GemmCfg{lds ? (q.BM == 256 ? wide_kind : 3) : 1, q.BM / 16, 4, 1, 4};
+    q.g1 = GemmCfg{lds ? (q.BM == 256 ? 2 : 3) : 1, q.BM / 16, 4, 1, 4};
     q.g2 = q.g1;
   }
 
