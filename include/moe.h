@@ -308,8 +308,10 @@ int moe_gemm1_act(const moe_problem* p, const void* x, const void* x_scale,
 /* Grouped GEMM2 and the routing-weighted combine ([GATED] sections 3-4:
  * FC2 non-gated, scatter unchanged; [TRTLLM]: bf16 output of x's shape).
  *   y_f     = topk_w[f] * dequant(W2[e] . a2[r]) for each real row r, kept
- *             in y_ws ([T*K'][H]) in fp32, or rounded to bf16 for W4A8
- *             (whose outputs the method holds to relative L2 3e-2)
+ *             in y_ws ([T*K'][H]) as fp32 rounded to nearest even at its
+ *             upper 24 bits (3 bytes a value: sign, exponent, 15 mantissa
+ *             bits), or rounded to bf16 for W4A8 (whose outputs the method
+ *             holds to relative L2 3e-2)
  *   out[t]  = bf16( sum over j with 0 <= topk_ids[t][j] < E of y_{t*K'+j} ),
  *             summed in slot order j = 0..K'-1, rounded once
  * out is written completely (rows with no valid slot become 0).

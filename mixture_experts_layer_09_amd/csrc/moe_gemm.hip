@@ -296,16 +296,16 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
   }
 }
 
-// out[t][:] = bf16(sum over valid slots j of y[t*K' + j][:]) with y in fp32
-// (BF: bf16, the rows of int4 weights), summed in fp32, one thread per 8
-// hidden values.  The rows of up to 8 slots are loaded
+// out[t][:] = bf16(sum over valid slots j of y[t*K' + j][:]) with y in 24-bit
+// codes (RB = 3) or bf16 (RB = 2, the rows of int4 weights), summed in fp32,
+// one thread per 8 hidden values.  The rows of up to 8 slots are loaded
 // before any is added, so each thread has 16 loads in flight; the sum still
 // runs in slot order.  Every slot's row lies inside y, so the rows are
 // loaded together with the ids rather than after them; a slot whose id is
 // outside [0, E) (never written by GEMM2) is loaded and left out of the sum.
 // (4 or 16 values per thread, or plain instead of non-temporal loads, were
 // measured slower.)
-template <bool BF>
+template <int RB>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
                                                      const void* __restrict__ yv,
                                                      uint16_t* __restrict__ out, int T, int H,
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       ok[u] = e >= 0 && e < E;
       if (j < Kp) {
         const size_t at = (size_t(t) * Kp + j) * H + c;
-        if constexpr (BF) {
+        if constexpr (RB == 2) {
           const u32x4 b = __builtin_nontemporal_load(
               reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(yv) + at));
 #pragma unroll
@@ -336,9 +336,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
             v[u][1][2 * k + 1] = bf16_to_f32(b[2 + k] >> 16);
           }
         } else {
-          const float* row = static_cast<const float*>(yv) + at;
-          v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row));
-          v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4));
+          // 24 bytes, 8-byte aligned (H is a multiple of 8): value i of a
+          // group of four in bytes 3i .. 3i + 2
+          const u32x2* row = reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(yv) + at * 3);
+          const u32x2 p0 = __builtin_nontemporal_load(row), p1 = __builtin_nontemporal_load(row + 1),
+                      p2 = __builtin_nontemporal_load(row + 2);
+          const uint32_t d[6] = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1]};
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t a = d[3 * h], b = d[3 * h + 1], c2 = d[3 * h + 2];
+            v[u][h][0] = f24_to_f32(a);
+            v[u][h][1] = f24_to_f32((a >> 24) | (b << 8));
+            v[u][h][2] = f24_to_f32((b >> 16) | (c2 << 16));
+            v[u][h][3] = f24_to_f32(c2 >> 8);
+          }
         }
       }
     }
@@ -362,11 +373,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 // GEMM2 and the combine in one kernel, token by token, for small batches: a
 // workgroup owns one token and 16 output channels and runs GEMM2 for each of
 // the token's slots -- the same fragments, k ranges and four-way K split as
-// gemm_stream<2, Q, 0, WT, 4>, so every slot's fp32 row is the one that
-// kernel writes -- then sums the routing-weighted rows in slot order and
-// rounds once to bf16, as combine_kernel does: the output is bit-identical to
-// gemm_stream<2> followed by combine_kernel, without the per-assignment rows
-// leaving the chip.  16 waves: wave w takes K quarter w % 4 of the slots
+// gemm_stream<2, Q, 0, WT, 4>, so every slot's row is the one that kernel
+// writes (rounded as it stores it) -- then sums the routing-weighted rows in
+// slot order and rounds once to bf16, as combine_kernel does: the output is
+// bit-identical to gemm_stream<2> followed by combine_kernel, without the
+// per-assignment rows leaving the chip.  16 waves: wave w takes K quarter w % 4 of the slots
 // (w / 4), (w / 4) + 4, ..., so that a wave has all its k-steps in flight at
 // once.  The padded row of each slot's intermediate is found by a scan of
 // sorted_ids.  Each weight tile a token routes to is streamed for that token
@@ -525,13 +536,12 @@ __global__ __launch_bounds__(1024) void gemm2_combine_tok(GemmArgs g, const int3
         f32x4 a = red[0][j][grp];
 #pragma unroll
         for (int k = 1; k < KS; ++k) a += red[k][j][grp];
-        // the row value first (as GEMM2 stores it, bf16 for int4 weights),
-        // then the slot-order sum: kept apart so that no fused multiply-add
-        // changes the rounding
+        // the row value first, rounded as GEMM2 stores it (bf16 for int4
+        // weights, 24 bits otherwise), then the slot-order sum: kept apart
+        // so that no fused multiply-add changes the rounding
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float r = __fmul_rn(a[i], wgt);
-          if (kRowsBf16<Q>) r = bf16_to_f32(bf16_bits(r));
+          const float r = row_round<Q>(__fmul_rn(a[i], wgt));
           sum[i] = __fadd_rn(sum[i], r);
         }
       }
@@ -729,11 +739,11 @@ hipError_t launch_combine(const moe_problem& p, const Plan& q, const int32_t* to
   const int64_t n = int64_t(p.T) * (p.H / 8);
   if (n == 0) return hipSuccess;
   if (rows_bf16(p.quant))
-    combine_kernel<true><<<unsigned((n + 255) / 256), 256, 0, stream>>>(topk_ids, y, out, p.T,
-                                                                      p.H, q.Kp, p.E);
+    combine_kernel<2><<<unsigned((n + 255) / 256), 256, 0, stream>>>(topk_ids, y, out, p.T, p.H,
+                                                                   q.Kp, p.E);
   else
-    combine_kernel<false><<<unsigned((n + 255) / 256), 256, 0, stream>>>(topk_ids, y, out, p.T,
-                                                                       p.H, q.Kp, p.E);
+    combine_kernel<3><<<unsigned((n + 255) / 256), 256, 0, stream>>>(topk_ids, y, out, p.T, p.H,
+                                                                   q.Kp, p.E);
   return hipGetLastError();
 }
 

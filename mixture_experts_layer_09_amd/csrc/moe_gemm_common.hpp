@@ -85,13 +85,34 @@ __device__ __forceinline__ i32x8 fp8_pair(const u32x4& lo, const u32x4& hi) {
   return r;
 }
 
-// GEMM2's per-assignment rows, summed by the combine: fp32, or bf16 for int4
+// GEMM2's per-assignment rows, summed by the combine.  bf16 for int4
 // weights (W4A8), whose outputs the method holds to a relative L2 error of
-// 3e-2 only -- rounding the ~8 weighted rows of a token to bf16 adds ~1e-3 --
-// so that the rows' round trip through HBM moves half the bytes.
+// 3e-2 only -- rounding the ~8 weighted rows of a token to bf16 adds ~1e-3.
+// Otherwise fp32 rounded to nearest even at its upper 24 bits (sign, the full
+// exponent, 15 mantissa bits: relative error <= 2^-16 per row, ~1e-4 of an
+// output at most against the 2e-2 bound) and stored in 3 bytes, so that the
+// rows' round trip through HBM moves three quarters of fp32's bytes.
 template <int Q> constexpr bool kRowsBf16 = rows_bf16(Q);
 
-// Four consecutive values of row f (element n) of the per-assignment rows y.
+// The 24-bit row code of v (NaN stays NaN, overflow rounds to infinity).
+__device__ __forceinline__ uint32_t f24_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 8) | ((u & 0x7FFFFFu) ? 0x4000u : 0u);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ float f24_to_f32(uint32_t code) { return __uint_as_float(code << 8); }
+
+// The value GEMM2 stores for v.
+template <int Q>
+__device__ __forceinline__ float row_round(float v) {
+  if constexpr (kRowsBf16<Q>) return bf16_to_f32(bf16_bits(v));
+  else return f24_to_f32(f24_bits(v));
+}
+
+// Four consecutive values of row f (element n, a multiple of 4) of the
+// per-assignment rows y: 8 bytes (bf16) or 12 (24-bit codes, value i in bytes
+// 3i .. 3i + 2, little-endian; three 4-byte stores, the address being a
+// multiple of 4 only).
 template <int Q>
 __device__ __forceinline__ void store_row4(uint8_t* y, size_t f, int H, int n, const f32x4& v) {
   if constexpr (kRowsBf16<Q>) {
@@ -100,7 +121,12 @@ __device__ __forceinline__ void store_row4(uint8_t* y, size_t f, int H, int n, c
     o[1] = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
     *reinterpret_cast<u32x2*>(y + (f * H + n) * 2) = o;
   } else {
-    *reinterpret_cast<f32x4*>(y + (f * H + n) * 4) = v;
+    const uint32_t c0 = f24_bits(v[0]), c1 = f24_bits(v[1]), c2 = f24_bits(v[2]),
+                   c3 = f24_bits(v[3]);
+    uint32_t* d = reinterpret_cast<uint32_t*>(y + (f * H + n) * 3);
+    d[0] = c0 | (c1 << 24);
+    d[1] = (c1 >> 8) | (c2 << 16);
+    d[2] = (c2 >> 16) | (c3 << 8);
   }
 }
 

@@ -209,7 +209,7 @@ int make_plan(const moe_problem* p, Plan* plan) {
 
   // ---- scratch sizes and the moe_forward workspace layout
   q.align_ws = q.chunks > 1 ? align256(size_t(q.chunks) * p->E * 4) : 256;
-  q.combine_ws = align256(size_t(q.A) * p->H * (rows_bf16(p->quant) ? 2 : 4));
+  q.combine_ws = align256(size_t(q.A) * p->H * row_bytes(p->quant));
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align256(std::max<size_t>(bytes, 1)); return at; };
   q.off_ids = take(size_t(q.A) * 4);

@@ -22,8 +22,10 @@ constexpr int kTokMaxAssign = 64;  // GEMM2 runs token by token up to this many 
 constexpr int kTokMaxTokens = 2;   // and tokens (measured: 8 tokens ran slower that way)
 constexpr int64_t kChunkAssign = 65536;  // moe_forward passes over at most this many assignments
 
-// GEMM2's per-assignment rows are bf16 for int4 weights (W4A8), fp32 otherwise.
+// GEMM2's per-assignment rows are bf16 for int4 weights (W4A8), otherwise
+// fp32 rounded to its upper 24 bits (sign, exponent, 15 mantissa bits).
 constexpr bool rows_bf16(int quant) { return quant == MOE_QUANT_W4A8; }
+constexpr int row_bytes(int quant) { return rows_bf16(quant) ? 2 : 3; }
 
 // The OCP MX modes (E8M0 scales per 32 K on weights and activations).
 inline bool quant_is_mx(int q) { return q == MOE_QUANT_MXFP8 || q == MOE_QUANT_MXFP4; }

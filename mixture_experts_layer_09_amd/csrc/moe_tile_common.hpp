@@ -12,7 +12,7 @@ namespace moe {
 // GEMM1 dequantises, applies the activation and stores the half-width rows
 // (fp8-block: per token and 128 channels s = amax / 448 across the waves,
 // through `lds_amax` [4][BM]); GEMM2 dequantises, applies the routing weight
-// and writes the assignments' fp32 rows.
+// and writes the assignments' rows (24-bit codes, or bf16 for int4 weights).
 template <int PHASE, int Q, int ACT, int WT, int NT>
 __device__ __forceinline__ void tiled_epilogue(const GemmArgs& g, f32x4 (&acc)[WT][NT], int e,
                                                int row0, int ct, int tile0, bool active,

@@ -136,7 +136,7 @@ def test_capacity_bounds(plan, T, K, E):
     assert nb == min(A, (A + min(E, A) * (bm - 1)) // bm)
     assert plan.moe_max_padded_rows(ctypes.byref(p)) == nb * bm
     ws = plan.moe_workspace_bytes(ctypes.byref(p))
-    assert ws >= A * 2048 * 4 + nb * bm * 768 * 2  # fp32 y rows + intermediate at least
+    assert ws >= A * 2048 * 3 + nb * bm * 768 * 2  # 24-bit y rows + intermediate at least
 
 
 def test_packed_bytes(plan):
@@ -223,6 +223,19 @@ def test_noalloc_capacity_and_rejection():
                     quant="fp8_tensor")):
         p = P(**kw)
         assert moe.lib.moe_workspace_bytes(ctypes.byref(p)) <= moe.NOALLOC_WORKSPACE_BYTES
+
+
+def test_combine_rows_take_three_bytes_a_value(plan):
+    """GEMM2's per-assignment rows: 3 bytes a value (fp32 rounded to 24
+    bits), 2 (bf16) for int4 weights; the combine workspace is exactly that,
+    rounded up to 256 bytes."""
+    cws = lambda **kw: plan.moe_combine_workspace_bytes(ctypes.byref(P(**kw)))
+    r256 = lambda v: (v + 255) // 256 * 256
+    for quant, b in (("bf16", 3), ("fp8_tensor", 3), ("fp8_block", 3), ("mxfp8", 3),
+                     ("mxfp4", 3), ("w4a8", 2)):
+        for T in (1, 37, 4096):
+            assert cws(T=T, H=2048, I=768, E_routed=128, top_k=8, quant=quant) == \
+                r256(T * 8 * 2048 * b), (quant, T)
 
 
 def test_workspace_stops_growing_past_one_pass(plan):
