@@ -394,6 +394,7 @@ __global__ __launch_bounds__(1024) void gemm2_combine_tok(GemmArgs g, const int3
   __shared__ int slot_row[KS * SG * KMAX];  // per wave: padded row of each slot
   __shared__ float slot_wgt[KMAX];
   __shared__ f32x4 red[KS][KMAX][4];  // the 4 lanes holding column 0, per K quarter and slot
+  __shared__ f32x4 rowv[KMAX][4];     // each valid slot's row (16 channels), in slot order
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4;
   const int kq = wave % KS, sg = wave / KS;
@@ -520,32 +521,39 @@ __global__ __launch_bounds__(1024) void gemm2_combine_tok(GemmArgs g, const int3
       if ((lane & 15) == 0) red[kq][j][grp] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   __syncthreads();
-  // ---- K-split partial sums in quarter order, routing weight, slot-order sum
-  // (wave 0; the lanes holding column 0 accumulate, the loop is uniform)
-  if (wave == 0) {
-    const bool col0 = (lane & 15) == 0;
+  // ---- each valid slot's row, one wave per slot (the lanes holding column
+  // 0): K-split partial sums in quarter order, routing weight, rounded as
+  // GEMM2 stores it (bf16 for int4 weights, 24 bits otherwise) -- the
+  // product kept apart from any sum so that no fused multiply-add changes
+  // the rounding
+  const bool col0 = (lane & 15) == 0;
+  for (int q = wave; q < nv; q += KS * SG) {  // uniform per wave
+    const int j = nth_slot(q);
+    const int e = __shfl(my_e, j, 64);
     float alpha = 1.f;
-    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < nv; ++q) {
-      const int j = nth_slot(q);
-      const int e = __shfl(my_e, j, 64);
-      if (Q == MOE_QUANT_FP8_TENSOR) alpha = g.w_scale[e] * *g.a2;
-      if (Q == MOE_QUANT_W4A8) alpha = *g.a2;
-      const float wgt = alpha * slot_wgt[j];
-      if (col0) {
-        f32x4 a = red[0][j][grp];
+    if (Q == MOE_QUANT_FP8_TENSOR) alpha = g.w_scale[e] * *g.a2;
+    if (Q == MOE_QUANT_W4A8) alpha = *g.a2;
+    const float wgt = alpha * slot_wgt[j];
+    if (col0) {
+      f32x4 a = red[0][j][grp];
 #pragma unroll
-        for (int k = 1; k < KS; ++k) a += red[k][j][grp];
-        // the row value first, rounded as GEMM2 stores it (bf16 for int4
-        // weights, 24 bits otherwise), then the slot-order sum: kept apart
-        // so that no fused multiply-add changes the rounding
+      for (int k = 1; k < KS; ++k) a += red[k][j][grp];
+      f32x4 r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float r = row_round<Q>(__fmul_rn(a[i], wgt));
-          sum[i] = __fadd_rn(sum[i], r);
-        }
-      }
+      for (int i = 0; i < 4; ++i) r[i] = row_round<Q>(__fmul_rn(a[i], wgt));
+      rowv[q][grp] = r;
     }
+  }
+  __syncthreads();
+  // ---- the slot-order sum (wave 0), rounded once to bf16
+  if (wave == 0) {
+    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (col0)
+      for (int q = 0; q < nv; ++q) {
+        const f32x4 r = rowv[q][grp];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] = __fadd_rn(sum[i], r[i]);
+      }
     if (col0) {
       u32x2 o;
       o[0] = bf16_bits(sum[0]) | (bf16_bits(sum[1]) << 16);

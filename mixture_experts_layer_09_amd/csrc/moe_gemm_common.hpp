@@ -94,11 +94,13 @@ __device__ __forceinline__ i32x8 fp8_pair(const u32x4& lo, const u32x4& hi) {
 // rows' round trip through HBM moves three quarters of fp32's bytes.
 template <int Q> constexpr bool kRowsBf16 = rows_bf16(Q);
 
-// The 24-bit row code of v (NaN stays NaN, overflow rounds to infinity).
+// The 24-bit row code of v: round to nearest even at bit 8 (a carry into
+// the exponent is the correct rounding, up to infinity); a NaN keeps its
+// upper bits with the quiet bit set, so that no payload is rounded away.
 __device__ __forceinline__ uint32_t f24_bits(float v) {
   const uint32_t u = __float_as_uint(v);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 8) | ((u & 0x7FFFFFu) ? 0x4000u : 0u);
-  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+  const uint32_t c = (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+  return v != v ? (u >> 8) | 0x4000u : c;
 }
 __device__ __forceinline__ float f24_to_f32(uint32_t code) { return __uint_as_float(code << 8); }
 
