@@ -399,19 +399,31 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ his
       }
     }
     __syncthreads();
+    // per expert, its chunks' counts: 8 LDS reads issued before their sum
     for (int x = threadIdx.x; x < E; x += kThreads) {
       int run = 0;
-      for (int c = 0; c < chunks; ++c) run += h[c * E + x];
+      for (int c0 = 0; c0 < chunks; c0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = c0 + u < chunks ? h[(c0 + u) * E + x] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) run += v[u];
+      }
       cnt[x] = run;
     }
     __syncthreads();
     padded_offsets(cnt, off, E, BM, tmp, g_offsets, g_npad);
     for (int x = threadIdx.x; x < E; x += kThreads) {
       int run = off[x];
-      for (int c = 0; c < chunks; ++c) {
-        const int v = h[c * E + x];
-        h[c * E + x] = run;
-        run += v;
+      for (int c0 = 0; c0 < chunks; c0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = c0 + u < chunks ? h[(c0 + u) * E + x] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (c0 + u < chunks) h[(c0 + u) * E + x] = run;
+          run += v[u];
+        }
       }
     }
     __syncthreads();
