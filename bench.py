@@ -26,7 +26,8 @@ HBM peak -- or, where its MFMA time at the nominal peaks exceeds its weight
 streaming time (prefill sizes), its algorithmic FLOPs to the dense MFMA peak
 of its dtype; ``roofline.layer`` does the same for the whole pass and the
 step time.  ``prefill`` times, with the default arguments, one moe_forward
-pass per step of the three prefill-sized workloads (fp8 block-scaled with
+pass per step (after untimed warm-up passes) of the three prefill-sized
+workloads (fp8 block-scaled with
 the shared expert at M = 4096 -- HBM-bound by its arithmetic intensity --,
 fp8 per-tensor relu^2 and W4A8 at M = 8192) and relates each pass and its
 GEMM1 to the fp8 MFMA peak (or HBM).  ``measured_peaks`` are the same
@@ -72,6 +73,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill-sized workloads' block")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-warmup", type=int, default=10,
+                    help="untimed passes of each prefill workload before its timed steps "
+                         "(2 left those passes 5-6%% short of their steady state)")
     ap.add_argument("--prefill-workloads", default="cfg3_M4096,cfg4_M8192,cfg5_M8192")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter scaling)")
@@ -444,7 +448,7 @@ def prefill_block(args):
         out = torch.empty((M, cfg.H), dtype=torch.bfloat16, device="cuda")
         ids = torch.empty((M, cfg.K_slots), dtype=torch.int32, device="cuda")
         gen_s = time.perf_counter() - t_gen
-        for _ in range(2):
+        for _ in range(args.prefill_warmup):
             layer.forward(x, lg, topk_ids=ids, out=out)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -459,6 +463,7 @@ def prefill_block(args):
         roof, _, _, _ = roofline(cfg, alg, g1, name)
         lay = layer_roofline(cfg, alg, ms)
         res.append({"workload": workload_text(cfg, M), "key": name, "tokens": M,
+                    "steps": args.prefill_steps, "warmup": args.prefill_warmup,
                     "ms_per_step": round(ms, 4), "tokens_per_s": round(M / (ms * 1e-3), 1),
                     "tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 1),
                     "dtype": DTYPE.get(cfg.quant, "fp8"), "layer": lay,
