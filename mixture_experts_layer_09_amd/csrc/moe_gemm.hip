@@ -11,8 +11,9 @@
 // before anything leaves registers; only the I activated columns are stored,
 // in the compute format.
 // GEMM2 (flashinfer PR 4329 page, sections 3-4): y = W2[e] . a, scaled by the
-// routing weight, written per assignment in fp32; the combine then sums each
-// token's K' rows in slot order and rounds once to bf16.
+// routing weight, written per assignment (fp32 rounded to 24 bits, bf16 for
+// int4 weights); the combine then sums each token's K' rows in fp32 in slot
+// order and rounds once to bf16.
 //
 // MFMA operands: the weights are the A operand (16 weight rows per tile) and
 // the tokens the B operand (16 tokens per tile), so a block with a handful of
@@ -147,9 +148,12 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
   };
 
   if (active) {
+    // D stages in a ring; the r steps past the last whole group of D are
+    // loaded as the last group's stages free up (not one at a time, each
+    // waiting for its own load); steps are computed in k order throughout
     Stage<Q, WT> st[D];
     const int n = s1 - s0;
-    const int G = n / D;
+    const int G = n / D, r = n - G * D;
     if (G > 0) {
 #pragma unroll
       for (int d = 0; d < D; ++d) load(st[d], s0 + d);
@@ -162,12 +166,18 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs g) {
         }
       }
 #pragma unroll
-      for (int d = 0; d < D; ++d) compute(st[d]);
+      for (int d = 0; d < D; ++d) {
+        compute(st[d]);
+        if (d < r) load(st[d], s0 + G * D + d);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+        if (d < r) load(st[d], s0 + d);
     }
-    for (int s = s0 + G * D; s < s1; ++s) {
-      load(st[0], s);
-      compute(st[0]);
-    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < r) compute(st[d]);
   }
 
   // ---- K-split: the partial sums of waves kp > 0 join wave kp == 0
