@@ -556,13 +556,16 @@ hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* log
                            int32_t* scratch, hipStream_t stream, bool align) {
   if (!align && !logits && !quantise) return hipSuccess;  // nothing to do
   if (!prologue_fits(p, q)) {
+    // routing and quantisation in one launch when both run, then the alignment
     hipError_t err = hipSuccess;
-    if (logits) err = launch_route(p, logits, ids, w, stream);
+    const bool fused = logits && quantise;
+    if (fused) err = launch_route_quant(p, logits, ids, w, x, a1, xq, xs, stream);
+    else if (logits) err = launch_route(p, logits, ids, w, stream);
     if (err != hipSuccess) return err;
     if (align)
       err = launch_align(p, q, ids, sorted_ids, block_expert, offsets, num_padded, scratch,
                          stream);
-    if (err != hipSuccess || !quantise) return err;
+    if (err != hipSuccess || !quantise || fused) return err;
     return launch_quant_act(p, x, a1, xq, xs, stream);
   }
   PrologueArgs a{};

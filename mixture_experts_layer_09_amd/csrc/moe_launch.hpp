@@ -35,6 +35,12 @@ hipError_t launch_prologue(const moe_problem& p, const Plan& q, const float* log
 hipError_t launch_quant_act(const moe_problem& p, const uint16_t* x, const float* a1,
                             uint8_t* xq, void* xs, hipStream_t stream);
 
+// launch_route and launch_quant_act as one launch (their workgroups side by
+// side), for batches the decode-size prologue does not take.
+hipError_t launch_route_quant(const moe_problem& p, const float* logits, int32_t* ids, float* w,
+                              const uint16_t* x, const float* a1, uint8_t* xq, void* xs,
+                              hipStream_t stream);
+
 hipError_t launch_pack_w(const moe_problem& p, const Plan& q, int which, const void* src,
                          int32_t src_I, int32_t swap, const void* src_scale, void* dst,
                          void* dst_scale, hipStream_t stream);
