@@ -194,10 +194,17 @@ def test_prepare_route_align_bitexact(T, Er, k, ns, renorm, bm):
                                                ("w4a8", 8, 6144, 20, 8, 0),
                                                ("mxfp8", 8, 2048, 128, 8, 0),
                                                ("mxfp4", 64, 2048, 128, 8, 0),
-                                               ("mxfp8", 300, 2048, 512, 10, 1)])
+                                               ("mxfp8", 300, 2048, 512, 10, 1),
+                                               ("fp8_tensor", 1000, 4096, 128, 6, 0),
+                                               ("w4a8", 2049, 6144, 20, 8, 0),
+                                               ("mxfp4", 777, 2048, 128, 8, 0)])
 def test_prepare_quantise_equals_separate_calls(quant, T, H, Er, k, ns):
     """moe_prepare's fused routing + quantisation + alignment is bit-identical
-    to moe_route, moe_quant_act and moe_align called one after another."""
+    to moe_route, moe_quant_act and moe_align called one after another: in one
+    workgroup at decode sizes, and above them (T = 300 and up: more than 1024
+    assignments) with the routing and the quantisation in one launch -- a
+    token per wave (512 routed experts) or per 16-lane row (128 and 20), token
+    counts that leave the last routing workgroup partly empty."""
     say(f"prepare {quant} T={T}")
     rng = np.random.default_rng(T + H)
     lg = dev(rng.standard_normal((T, Er)).astype(np.float32))
