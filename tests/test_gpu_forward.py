@@ -358,6 +358,30 @@ def test_token_major_gemm2_equals_expert_major_path(quant, act):
            label=f"token-major {quant} {act}")
 
 
+@pytest.mark.parametrize("quant,act,k,ns,T", [("bf16", "silu", 40, 2, 1), ("fp8_tensor", "silu", 63, 1, 1),
+                                              ("w4a8", "silu", 30, 2, 2), ("mxfp8", "gelu_tanh", 28, 2, 2)])
+def test_token_major_gemm2_many_slots(quant, act, k, ns, T):
+    """The token-major GEMM2 with more valid slots than its 16 waves (each
+    wave forms the rows of slots w, w + 16, ...): T tokens of up to 64
+    assignments against the first T tokens of a batch one token larger
+    (expert-major GEMM2 and the combine), bit for bit, and the oracle (one
+    shared slot at most, so that |out| stays where the absolute 2e-2 bound
+    exceeds the bf16 rounding of the output itself)."""
+    cfg = ad_hoc(99, quant, act, H=256, I=256, E_routed=64, top_k=k, n_shared=ns)
+    W = synth.make_weights(cfg, seed=57)
+    tok = synth.make_tokens(cfg, T + 1, seed=58)
+    sc = synth.make_act_scales(cfg, tok["x_bits"])
+    layer = build_layer(cfg, W, sc["a1"], sc["a2"])
+    say(f"token-major many slots {quant} K'={k + ns} T={T}")
+    x, lg = dev(tok["x_bits"]), dev(tok["logits"])
+    few = layer.forward(x[:T].contiguous(), lg[:T].contiguous())
+    more = layer.forward(x, lg)
+    torch.cuda.synchronize()
+    assert torch.equal(few.view(torch.int16), more[:T].view(torch.int16))
+    parity(cfg, W, layer, tok["x_bits"][:T], tok["logits"][:T], sc["a1"], sc["a2"],
+           label=f"token-major many slots {quant}")
+
+
 @pytest.mark.parametrize("quant,routed", [("bf16", True), ("bf16", False), ("fp8_tensor", True),
                                           ("fp8_tensor", False), ("w4a8", False),
                                           ("mxfp4", True)])
