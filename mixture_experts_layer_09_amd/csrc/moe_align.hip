@@ -399,31 +399,33 @@ __global__ __launch_bounds__(kThreads) void align_scan(int32_t* __restrict__ his
       }
     }
     __syncthreads();
-    // per expert, its chunks' counts: 8 LDS reads issued before their sum
-    for (int x = threadIdx.x; x < E; x += kThreads) {
-      int run = 0;
-      for (int c0 = 0; c0 < chunks; c0 += 8) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = c0 + u < chunks ? h[(c0 + u) * E + x] : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) run += v[u];
-      }
-      cnt[x] = run;
+    // P consecutive lanes per expert (E <= 1024 = kThreads experts in one
+    // pass), each over a contiguous range of the chunks: the range's count,
+    // then a prefix over the expert's P lanes gives each range's start
+    const int P = E > kThreads / 2 ? 1 : E > kThreads / 4 ? 2 : E > kThreads / 8 ? 4
+                : E > kThreads / 16 ? 8 : 16;
+    const int lane = threadIdx.x & 63, x = threadIdx.x / P, part = threadIdx.x % P;
+    const bool own = x < E;
+    const int per = (chunks + P - 1) / P;
+    const int c0 = min(chunks, part * per), c1 = min(chunks, c0 + per);
+    int sum = 0;
+    if (own)
+      for (int c = c0; c < c1; ++c) sum += h[c * E + x];
+    int incl = sum;  // inclusive prefix over the expert's lanes (P divides 64)
+    for (int d = 1; d < P; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (part >= d) incl += o;
     }
+    const int total = __shfl(incl, lane - part + P - 1, 64);
+    if (own && part == 0) cnt[x] = total;
     __syncthreads();
     padded_offsets(cnt, off, E, BM, tmp, g_offsets, g_npad);
-    for (int x = threadIdx.x; x < E; x += kThreads) {
-      int run = off[x];
-      for (int c0 = 0; c0 < chunks; c0 += 8) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = c0 + u < chunks ? h[(c0 + u) * E + x] : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (c0 + u < chunks) h[(c0 + u) * E + x] = run;
-          run += v[u];
-        }
+    if (own) {
+      int run = off[x] + incl - sum;
+      for (int c = c0; c < c1; ++c) {
+        const int v = h[c * E + x];
+        h[c * E + x] = run;
+        run += v;
       }
     }
     __syncthreads();
